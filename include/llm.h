@@ -1,0 +1,215 @@
+/*
+ * llm.h -- C ABI of the MI355X (gfx950) Llama-2/3 decoder forward pass.
+ *
+ * The pass follows the model walked through on the pages
+ *   "Resumen de una implementación desde cero del modelo LLaMA-3" (GeekNews, es),
+ *   "Model Llama 3 yang Diimplementasikan dengan NumPy Murni" (GeekNews, id),
+ *   "Building llama3 from scratch" (downcodes, ar) and "LLaMA2" (downcodes, fr):
+ * token embedding -> n_layers x [RMSNorm -> separate wq/wk/wv projections ->
+ * RoPE on q and k -> KV-cache write -> causal grouped-query attention -> wo and
+ * residual add -> RMSNorm -> SwiGLU feed-forward (w1/w3 gate-up, w2 down) and
+ * residual add] -> final RMSNorm -> output projection (last position only in a
+ * prefill) -> greedy argmax.  Prefill runs a whole prompt; a decode step runs
+ * one new token per sequence against its KV cache ("Generasi" section of the
+ * NumPy page).
+ *
+ * Conventions shared by every call:
+ *  - Pointers documented as "device" point to GPU memory owned by the caller
+ *    (for example torch tensors).  The library never allocates or frees device
+ *    memory and keeps no device pointer beyond the buffers handed to
+ *    llm_init_weights.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every compute call only enqueues work on that stream and returns; results
+ *    are valid once the stream has been synchronised.  No call synchronises the
+ *    device except llm_init_weights (at its end) and llm_read_device_error.
+ *  - Matrices are row-major.  Weights are [out_features, in_features] and a
+ *    linear layer computes y = x W^T (printed shapes on the "Building llama3
+ *    from scratch" page: wq [4096, 4096], wk/wv [1024, 4096]).  Query head h
+ *    owns rows h*head_dim .. h*head_dim+head_dim-1 of wq (per-head view of wq on
+ *    the same page); K/V head g likewise owns rows of wk/wv.
+ *  - bf16 buffers hold raw bfloat16 bit patterns (uint16).
+ *  - Every call returns an llm_status.  Host-side validation happens before
+ *    anything is enqueued, so a failing call leaves the stream untouched.
+ *    llm_last_error_message() then describes the failure (thread-local).
+ *  - Values read on the device (token ids, decode positions and slots) are
+ *    bounds-checked by the kernels: an out-of-range entry makes that row
+ *    produce no cache write and zero output, and sets a flag readable with
+ *    llm_read_device_error().
+ */
+#ifndef LLM_H
+#define LLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum llm_status {
+  LLM_OK = 0,
+  LLM_ERR_INVALID_ARG = -1,      /* null pointer, negative size, bad dtype */
+  LLM_ERR_CONFIG = -2,           /* inconsistent hyper-parameters */
+  LLM_ERR_OUT_OF_RANGE = -3,     /* positions / slots / batch beyond the configured maxima */
+  LLM_ERR_BUFFER_TOO_SMALL = -4, /* a caller buffer is smaller than the size query returns */
+  LLM_ERR_HIP = -5               /* a HIP runtime call failed */
+} llm_status;
+
+/* Storage type of weights, activations and the KV cache. */
+enum { LLM_F32 = 0, LLM_BF16 = 1 };
+
+/* Device-side error flags (bit mask) reported by llm_read_device_error. */
+enum { LLM_DEVERR_TOKEN = 1, LLM_DEVERR_POSITION = 2, LLM_DEVERR_SLOT = 4 };
+
+/*
+ * Model hyper-parameters: the params.json field set printed on the "Building
+ * llama3 from scratch" page (dim, n_layers, n_heads, n_kv_heads, vocab_size,
+ * norm_eps, rope_theta) with the feed-forward width given explicitly instead of
+ * multiple_of / ffn_dim_multiplier, plus the context length (max_seq_len, NumPy
+ * page, "Struktur").  Requirements: dim % n_heads == 0; head_dim = dim/n_heads
+ * is a multiple of 16; n_heads % n_kv_heads == 0; dim and ffn_hidden_dim are
+ * multiples of 8 (bf16) or 4 (fp32).
+ * max_batch: number of KV-cache slots (= largest decode batch).
+ * max_prefill_tokens: largest n_tokens of one llm_prefill / llm_layer_forward.
+ */
+typedef struct llm_config {
+  int32_t dim;
+  int32_t n_layers;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t vocab_size;
+  int32_t max_seq_len;
+  int32_t ffn_hidden_dim;
+  float rope_theta;
+  float norm_eps;
+  int32_t dtype;              /* LLM_F32 or LLM_BF16 */
+  int32_t max_batch;
+  int32_t max_prefill_tokens;
+} llm_config;
+
+/*
+ * Device pointers to the weights, named as in the checkpoint listing on the
+ * "Building llama3 from scratch" page.  All have the config's dtype.  The
+ * per-layer members are HOST arrays of n_layers device pointers.  `norm` is the
+ * final RMSNorm weight and `output` the (untied) LM head; their names are not
+ * printed on the pages.
+ *   tok_embeddings [vocab, dim]      output [vocab, dim]      norm [dim]
+ *   attention_norm[l], ffn_norm[l] [dim]
+ *   wq[l] [n_heads*head_dim, dim]    wk[l], wv[l] [n_kv_heads*head_dim, dim]
+ *   wo[l] [dim, n_heads*head_dim]
+ *   w1[l], w3[l] [ffn_hidden_dim, dim]    w2[l] [dim, ffn_hidden_dim]
+ */
+typedef struct llm_weights {
+  const void* tok_embeddings;
+  const void* const* attention_norm;
+  const void* const* wq;
+  const void* const* wk;
+  const void* const* wv;
+  const void* const* wo;
+  const void* const* ffn_norm;
+  const void* const* w1;
+  const void* const* w3;
+  const void* const* w2;
+  const void* norm;
+  const void* output;
+} llm_weights;
+
+typedef struct llm_model llm_model;
+
+/* Check a configuration without touching the GPU.  LLM_OK or LLM_ERR_CONFIG. */
+llm_status llm_check_config(const llm_config* cfg);
+
+/* Sizes in bytes of the three device buffers llm_init_weights needs (0 if the
+ * config is invalid).  Packed weights: every weight plus the fp32 RoPE tables.
+ * KV cache: n_layers x {K,V} x max_batch x n_kv_heads x max_seq_len x head_dim.
+ * Workspace: activations for max(max_prefill_tokens, max_batch) rows and
+ * attention / argmax partials. */
+size_t llm_packed_weight_bytes(const llm_config* cfg);
+size_t llm_kv_cache_bytes(const llm_config* cfg);
+size_t llm_workspace_bytes(const llm_config* cfg);
+
+/*
+ * Validate `cfg`, copy and repack the weights into `packed` (q/k/v rows
+ * concatenated per layer, w1/w3 rows interleaved, norm weights widened to
+ * fp32), build the RoPE cos/sin tables (angle pos * rope_theta^(-2j/head_dim)
+ * from an fp64 outer product, "RoPE #1" on the NumPy page) and create a model
+ * handle in *out.  The three buffers must stay alive until llm_free; the
+ * source weights may be freed once this call returns.  The call synchronises
+ * `stream` before returning.  Errors: INVALID_ARG (null pointer), CONFIG,
+ * BUFFER_TOO_SMALL (a size below the corresponding query), HIP.
+ */
+llm_status llm_init_weights(const llm_config* cfg, const llm_weights* weights,
+                            void* packed, size_t packed_bytes,
+                            void* kv_cache, size_t kv_cache_bytes,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream, llm_model** out);
+
+/*
+ * Prefill ("Generasi": the whole prompt at once): embed tokens_dev[0..n_tokens)
+ * (device int32), run every layer at positions start_pos .. start_pos+n_tokens-1
+ * writing K/V into cache slot `slot`, and write the logits of the LAST position
+ * ("Linear": only the last logit is computed) to logits_dev (device fp32
+ * [vocab]).  Errors: INVALID_ARG, OUT_OF_RANGE (slot >= max_batch,
+ * n_tokens > max_prefill_tokens, start_pos + n_tokens > max_seq_len).
+ */
+llm_status llm_prefill(llm_model* m, int32_t slot, const int32_t* tokens_dev, int32_t n_tokens,
+                       int32_t start_pos, float* logits_dev, void* stream);
+
+/*
+ * One decoder layer on an explicit residual stream, used to test a layer on its
+ * own: x_dev (device fp32 [n_tokens, dim]) is updated in place to the layer's
+ * output, at positions start_pos.. and cache slot `slot`.  Same kernels and
+ * errors as llm_prefill (plus OUT_OF_RANGE for a bad layer index).
+ */
+llm_status llm_layer_forward(llm_model* m, int32_t layer, int32_t slot, float* x_dev,
+                             int32_t n_tokens, int32_t start_pos, void* stream);
+
+/*
+ * One decode step for `batch` independent sequences ("KV cache" and "Generasi"
+ * sections: only the newest token is fed, K/V of earlier tokens come from the
+ * cache).  Row b: slot slots_dev[b], new token tokens_dev[b] at position
+ * positions_dev[b] (= number of tokens already cached in that slot); its K/V
+ * are written at that position and attention covers positions 0..positions[b].
+ * All three arrays are device int32 [batch]; logits_dev is device fp32
+ * [batch, vocab].  Errors: INVALID_ARG, OUT_OF_RANGE (batch > max_batch);
+ * device-side range errors are flagged (see llm_read_device_error).
+ */
+llm_status llm_decode_step(llm_model* m, int32_t batch, const int32_t* slots_dev,
+                           const int32_t* positions_dev, const int32_t* tokens_dev,
+                           float* logits_dev, void* stream);
+
+/*
+ * Greedy choice ("Predicción de tokens": the token with the highest logit):
+ * out_dev[r] = argmax over logits_dev[r*vocab .. r*vocab+vocab-1], lowest index
+ * on ties.  logits_dev device fp32 [rows, vocab]; out_dev device int32 [rows].
+ * Needs no model.  Errors: INVALID_ARG.
+ */
+llm_status llm_argmax(const float* logits_dev, int32_t rows, int32_t vocab, int32_t* out_dev,
+                      void* stream);
+
+/*
+ * Greedy generation on the device: `n_steps` times { decode step for `batch`
+ * rows; argmax into tokens_dev; positions_dev[b] += 1; out_tokens_dev[s*batch+b]
+ * = new token }.  tokens_dev / positions_dev are updated in place; logits_dev
+ * (device fp32 [batch, vocab]) holds the last step's logits.  One step is
+ * captured once into a HIP graph per (batch, buffers) and replayed.  Errors as
+ * llm_decode_step.
+ */
+llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev,
+                        int32_t* positions_dev, int32_t* tokens_dev, int32_t n_steps,
+                        int32_t* out_tokens_dev, float* logits_dev, void* stream);
+
+/* Synchronise `stream`, then return (and clear) the device error flags
+ * (LLM_DEVERR_* bits) in *flags.  Errors: INVALID_ARG, HIP. */
+llm_status llm_read_device_error(llm_model* m, int32_t* flags, void* stream);
+
+/* Release the host-side handle (no device memory is freed). NULL is allowed. */
+void llm_free(llm_model* m);
+
+const char* llm_status_string(llm_status s);
+const char* llm_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLM_H */

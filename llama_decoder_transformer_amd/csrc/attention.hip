@@ -1,0 +1,434 @@
+// Causal grouped-query attention over the KV cache.
+//
+// Scores are q.k / sqrt(d) over the keys at positions <= the query's position,
+// softmax, then the weighted sum of the values; query head h reads KV head
+// h / (n_heads / n_kv_heads) ("Scaled Dot-Product Attention" and "GQA" sections
+// of the NumPy page; attention / mask / softmax bullets of the Spanish summary).
+// Both kernels use the online (running-max) softmax, which reaches the same
+// result as the plain softmax; scores are kept in the log2 domain so the
+// exponentials are exp2.
+//
+// Cache layout (per layer, per K/V): [slot][kv_head][max_seq][head_dim].
+#include "common.h"
+#include "launch.h"
+
+namespace llm {
+
+constexpr float LOG2E_F = 1.4426950408889634f;
+
+// ============================================================== split-KV decode
+//
+// Grid (chunk, kv-head x head-block, row).  A workgroup handles one row (decode
+// sequence or prefill token), one KV head, up to 4 of its query heads, and the
+// CH keys of one chunk; 16 groups of 16 lanes each take one key at a time, a
+// lane holding d/16 elements (16 bytes for bf16 d = 128).  Each group keeps its
+// own running max / sum / accumulator; the 16 groups are merged through LDS and
+// written as a partial (max, sum, acc[d]) that attn_combine merges over chunks.
+
+constexpr int DEC_MAXH = 4;
+
+template <typename T, int EPL>
+__device__ __forceinline__ void load_epl(const T* p, float* out) {
+  if constexpr (EPL == 8) {
+    load8(p, out);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = to_f32<T>(p[e]);
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc,
+                                                          const T* __restrict__ vc, const int* __restrict__ row_pos,
+                                                          const int* __restrict__ row_slot, int pos0, int slot0,
+                                                          int H, int G, int max_seq, int n_slots, int CH, int nchunks,
+                                                          int hpb, float* __restrict__ partial) {
+  constexpr int EPL = D / 16;
+  __shared__ float s_m[16][DEC_MAXH];
+  __shared__ float s_l[16][DEC_MAXH];
+  __shared__ float s_acc[16][DEC_MAXH][D];
+
+  const int chunk = blockIdx.x, gy = blockIdx.y, row = blockIdx.z;
+  const int hpg = H / G;
+  const int nhb = hpg / hpb;
+  const int g = gy / nhb;
+  const int h0 = g * hpg + (gy % nhb) * hpb;
+  const int pos = row_pos ? row_pos[row] : pos0 + row;
+  const int slot = row_slot ? row_slot[row] : slot0;
+  if (pos < 0 || pos >= max_seq || slot < 0 || slot >= n_slots) return;
+  const int start = chunk * CH;
+  if (start > pos) return;
+  const int end = min(pos + 1, start + CH);
+
+  const int tid = threadIdx.x, grp = tid >> 4, gl = tid & 15;
+  const float scale = LOG2E_F / sqrtf((float)D);
+
+  float qv[DEC_MAXH][EPL];
+#pragma unroll
+  for (int hh = 0; hh < DEC_MAXH; ++hh) {
+    if (hh < hpb) {
+      load_epl<T, EPL>(q + (size_t)row * H * D + (size_t)(h0 + hh) * D + gl * EPL, qv[hh]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[hh][e] *= scale;
+    }
+  }
+  float mx[DEC_MAXH], sm[DEC_MAXH], acc[DEC_MAXH][EPL];
+#pragma unroll
+  for (int hh = 0; hh < DEC_MAXH; ++hh) {
+    mx[hh] = -1e30f;
+    sm[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
+  }
+
+  const size_t base = ((size_t)slot * G + g) * (size_t)max_seq * D;
+  const T* kb = kc + base;
+  const T* vb = vc + base;
+  for (int j = start + grp; j < end; j += 16) {
+    float kv[EPL], vv[EPL];
+    load_epl<T, EPL>(kb + (size_t)j * D + gl * EPL, kv);
+    load_epl<T, EPL>(vb + (size_t)j * D + gl * EPL, vv);
+#pragma unroll
+    for (int hh = 0; hh < DEC_MAXH; ++hh) {
+      if (hh < hpb) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qv[hh][e], kv[e], s);
+        s += __shfl_xor(s, 8);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 1);
+        const float mn = fmaxf(mx[hh], s);
+        const float alpha = exp2f(mx[hh] - mn);
+        const float p = exp2f(s - mn);
+        sm[hh] = sm[hh] * alpha + p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(p, vv[e], acc[hh][e] * alpha);
+        mx[hh] = mn;
+      }
+    }
+  }
+
+#pragma unroll
+  for (int hh = 0; hh < DEC_MAXH; ++hh) {
+    if (hh < hpb) {
+      if (gl == 0) { s_m[grp][hh] = mx[hh]; s_l[grp][hh] = sm[hh]; }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[grp][hh][gl * EPL + e] = acc[hh][e];
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < hpb * D; t += 256) {
+    const int hh = t / D, e = t % D;
+    float M = -1e30f;
+    for (int i = 0; i < 16; ++i) M = fmaxf(M, s_m[i][hh]);
+    float L = 0.f, a = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      const float w = exp2f(s_m[i][hh] - M);
+      L += s_l[i][hh] * w;
+      a += s_acc[i][hh][e] * w;
+    }
+    float* pr = partial + (((size_t)row * H + h0 + hh) * nchunks + chunk) * (D + 2);
+    pr[e] = a;
+    if (e == 0) { pr[D] = M; pr[D + 1] = L; }
+  }
+}
+
+// Merge the chunk partials of one (row, head): o = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M).
+template <typename T, int D>
+__global__ void attn_combine_kernel(const float* __restrict__ partial, const int* __restrict__ row_pos,
+                                    const int* __restrict__ row_slot, int pos0, int slot0, int H, int max_seq,
+                                    int n_slots, int CH, int nchunks, T* __restrict__ out, int* err) {
+  const int h = blockIdx.x, row = blockIdx.y, e = threadIdx.x;
+  const int pos = row_pos ? row_pos[row] : pos0 + row;
+  const int slot = row_slot ? row_slot[row] : slot0;
+  T* o = out + (size_t)row * H * D + (size_t)h * D;
+  if (pos < 0 || pos >= max_seq || slot < 0 || slot >= n_slots) {
+    if (e < D) o[e] = from_f32<T>(0.f);
+    if (e == 0 && h == 0) atomicOr(err, pos < 0 || pos >= max_seq ? 2 : 4);
+    return;
+  }
+  const int nv = pos / CH + 1;
+  const float* pr = partial + ((size_t)row * H + h) * nchunks * (D + 2);
+  float M = -1e30f;
+  for (int c = 0; c < nv; ++c) M = fmaxf(M, pr[(size_t)c * (D + 2) + D]);
+  float L = 0.f, a = 0.f;
+  for (int c = 0; c < nv; ++c) {
+    const float* pc = pr + (size_t)c * (D + 2);
+    const float w = exp2f(pc[D] - M);
+    L += pc[D + 1] * w;
+    if (e < D) a += pc[e] * w;
+  }
+  if (e < D) o[e] = from_f32<T>(a / L);
+}
+
+int attn_decode_chunk(int rows, int n_kv_heads, int max_seq) {
+  int ch = 512;
+  while (ch > 64 && (long)rows * n_kv_heads * ((max_seq + ch - 1) / ch) < 2048) ch >>= 1;
+  return ch;
+}
+
+size_t attn_decode_partial_floats(int rows, int n_heads, int head_dim, int max_seq) {
+  const int nch = (max_seq + 63) / 64;
+  return (size_t)rows * n_heads * nch * (head_dim + 2);
+}
+
+template <typename T, int D>
+static void attn_decode_dispatch(const T* q, const T* kc, const T* vc, const int* row_pos, const int* row_slot,
+                                 int pos0, int slot0, int rows, int H, int G, int max_seq, int n_slots,
+                                 float* partial, T* out, int* err, hipStream_t s) {
+  const int CH = attn_decode_chunk(rows, G, max_seq);
+  const int nch = (max_seq + CH - 1) / CH;
+  const int hpg = H / G;
+  const int hpb = hpg <= DEC_MAXH ? hpg : DEC_MAXH;
+  dim3 grid(nch, G * (hpg / hpb), rows);
+  attn_decode_kernel<T, D><<<grid, 256, 0, s>>>(q, kc, vc, row_pos, row_slot, pos0, slot0, H, G, max_seq, n_slots,
+                                               CH, nch, hpb, partial);
+  attn_combine_kernel<T, D><<<dim3(H, rows), D < 64 ? 64 : D, 0, s>>>(partial, row_pos, row_slot, pos0, slot0, H,
+                                                                      max_seq, n_slots, CH, nch, out, err);
+}
+
+void launch_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache, const int* row_pos,
+                        const int* row_slot, int pos0, int slot0, int rows, int n_heads, int n_kv_heads,
+                        int head_dim, int max_seq, int n_slots, float* partial, void* out, int* err,
+                        hipStream_t s) {
+  if (rows <= 0) return;
+#define LLM_DEC(T, D)                                                                                        \
+  attn_decode_dispatch<T, D>((const T*)q, (const T*)k_cache, (const T*)v_cache, row_pos, row_slot, pos0, slot0, \
+                             rows, n_heads, n_kv_heads, max_seq, n_slots, partial, (T*)out, err, s)
+  if (dtype == 1) {
+    if (head_dim == 128) LLM_DEC(bf16_t, 128);
+    else if (head_dim == 64) LLM_DEC(bf16_t, 64);
+    else LLM_DEC(bf16_t, 48);
+  } else {
+    if (head_dim == 128) LLM_DEC(float, 128);
+    else if (head_dim == 64) LLM_DEC(float, 64);
+    else LLM_DEC(float, 48);
+  }
+#undef LLM_DEC
+}
+
+// ============================================================== MFMA prefill
+//
+// bf16, head_dim 128.  Grid (query block, kv-head x head-block).  A workgroup
+// holds 4 waves; each wave owns 32 queries of one query head, and the waves of
+// a workgroup share one KV head so a K/V tile of 64 keys is staged in LDS once
+// for all of them (GQA packing: 4 query heads x 32 queries when the group has 4
+// or more heads).  Heaviest causal blocks are scheduled first.
+//
+// Per 64-key tile a wave computes S^T = K Q^T (keys as MFMA rows, queries as
+// columns), so each lane's accumulators all belong to one query column: the
+// softmax max needs only two cross-lane steps and the scaled probabilities,
+// packed to bf16, are already the B operand of O^T += V^T P^T.  The k-order of
+// that second product is the permutation {4g..4g+3, 16+4g..16+4g+3} of each
+// 32-key slice that the first product leaves in lane group g; the V^T operand is
+// read from a transposed LDS copy of V in the same order.
+
+constexpr int PF_D = 128;
+constexpr int PF_KT = 64;
+constexpr int PF_KLD = PF_D + 8;   // Ks row: 272 bytes
+constexpr int PF_VLD = PF_KT + 8;  // Vt row: 144 bytes
+
+template <int HPW>
+__global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
+                                                           const bf16_t* __restrict__ vc, int slot, int pos0, int S,
+                                                           int H, int G, int max_seq, bf16_t* __restrict__ out) {
+  constexpr int QSUB = 4 / HPW;  // 32-query sub-blocks per workgroup
+  constexpr int QB = 32 * QSUB;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[PF_KT * PF_KLD];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[PF_D * PF_VLD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int hpg = H / G;
+  const int nhb = hpg / HPW;
+  const int qblk = gridDim.x - 1 - blockIdx.x;
+  const int g = blockIdx.y / nhb;
+  const int head = g * hpg + (blockIdx.y % nhb) * HPW + (wid % HPW);
+  const int qw0 = qblk * QB + 32 * (wid / HPW);  // first query row of this wave
+  const int wg_last = min(S, qblk * QB + QB) - 1;
+  const int kv_end = pos0 + wg_last + 1;           // keys [0, kv_end) can be seen
+  const int ld_q = H * PF_D;
+  const float scale = LOG2E_F / sqrtf((float)PF_D);
+
+  // Q fragments (B operand): column = query jq*16 + l16, k = 32 s + 8 lg .. +7.
+  bf16x8_t qf[2][4];
+#pragma unroll
+  for (int jq = 0; jq < 2; ++jq) {
+    const int i = qw0 + jq * 16 + l16;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      u32x4_t raw = {0u, 0u, 0u, 0u};
+      if (i < S) raw = *reinterpret_cast<const u32x4_t*>(q + (size_t)i * ld_q + head * PF_D + s4 * 32 + lg * 8);
+      qf[jq][s4] = __builtin_bit_cast(bf16x8_t, raw);
+    }
+  }
+
+  f32x4_t o[8][2];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int jq = 0; jq < 2; ++jq) o[mb][jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrow[2] = {-1e30f, -1e30f}, lrow[2] = {0.f, 0.f};
+
+  const size_t base = ((size_t)slot * G + g) * (size_t)max_seq * PF_D;
+  const bf16_t* kb = kc + base;
+  const bf16_t* vb = vc + base;
+  const int ntiles = (kv_end + PF_KT - 1) / PF_KT;
+  const int wave_last_pos = pos0 + qw0 + 31;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * PF_KT;
+    __syncthreads();
+    // K tile: 16 lanes per key row (coalesced), straight copy.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + i * 256, key = idx >> 4, c = idx & 15;
+      u32x4_t raw = {0u, 0u, 0u, 0u};
+      if (k0 + key < kv_end) raw = *reinterpret_cast<const u32x4_t*>(kb + (size_t)(k0 + key) * PF_D + c * 8);
+      *reinterpret_cast<u32x4_t*>(&Ks[key * PF_KLD + c * 8]) = raw;
+    }
+    // V tile, transposed to Vt[d][key]: consecutive lanes take consecutive keys.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + i * 256, key = idx & 63, c = idx >> 6;
+      u32x4_t raw = {0u, 0u, 0u, 0u};
+      if (k0 + key < kv_end) raw = *reinterpret_cast<const u32x4_t*>(vb + (size_t)(k0 + key) * PF_D + c * 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        Vt[(c * 8 + 2 * w) * PF_VLD + key] = (bf16_t)(raw[w] & 0xFFFFu);
+        Vt[(c * 8 + 2 * w + 1) * PF_VLD + key] = (bf16_t)(raw[w] >> 16);
+      }
+    }
+    __syncthreads();
+    if (k0 > wave_last_pos) continue;  // every key of this tile is in this wave's future
+
+    // S^T = K Q^T : st[kb][jq][r] = score(key k0 + 16 kb + 4 lg + r, query jq*16 + l16)
+    f32x4_t st[4][2];
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+      for (int jq = 0; jq < 2; ++jq) st[kb4][jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(&Ks[(kb4 * 16 + l16) * PF_KLD + s4 * 32 + lg * 8]);
+#pragma unroll
+        for (int jq = 0; jq < 2; ++jq)
+          st[kb4][jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[jq][s4], st[kb4][jq], 0, 0, 0);
+      }
+    }
+
+    // Online softmax per query column.
+    bf16x8_t pf[2][2];  // [jq][k-step of 32 keys]
+#pragma unroll
+    for (int jq = 0; jq < 2; ++jq) {
+      const int qpos = pos0 + qw0 + jq * 16 + l16;
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + kb4 * 16 + lg * 4 + r;
+          float v = st[kb4][jq][r] * scale;
+          if (key > qpos) v = -INFINITY;
+          st[kb4][jq][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mn = fmaxf(mrow[jq], tmax);
+      const float alpha = exp2f(mrow[jq] - mn);
+      mrow[jq] = mn;
+      float psum = 0.f;
+      uint32_t packed[2][4];
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = exp2f(st[kb4][jq][r] - mn);
+          psum += p[r];
+        }
+        // k-step kb4/2 holds blocks 2t (elements 0..3) and 2t+1 (elements 4..7).
+        const int ks = kb4 >> 1, half = (kb4 & 1) * 2;
+        packed[ks][half] = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
+        packed[ks][half + 1] = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
+      }
+      lrow[jq] = lrow[jq] * alpha + psum;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) o[mb][jq] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4_t u = {packed[ks][0], packed[ks][1], packed[ks][2], packed[ks][3]};
+        pf[jq][ks] = __builtin_bit_cast(bf16x8_t, u);
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const bf16_t* vrow = &Vt[(mb * 16 + l16) * PF_VLD + ks * 32 + lg * 4];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        u32x4_t u = {lo.x, lo.y, hi.x, hi.y};
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u);
+#pragma unroll
+        for (int jq = 0; jq < 2; ++jq)
+          o[mb][jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[jq][ks], o[mb][jq], 0, 0, 0);
+      }
+    }
+  }
+
+  // Normalise and store: lane holds d = 16 mb + 4 lg + r of query jq*16 + l16.
+#pragma unroll
+  for (int jq = 0; jq < 2; ++jq) {
+    float L = lrow[jq];
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    const float inv = 1.0f / L;
+    const int i = qw0 + jq * 16 + l16;
+    if (i < S) {
+      bf16_t* orow = out + (size_t)i * ld_q + head * PF_D;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        uint2 w;
+        w.x = (uint32_t)f32_to_bf16(o[mb][jq][0] * inv) | ((uint32_t)f32_to_bf16(o[mb][jq][1] * inv) << 16);
+        w.y = (uint32_t)f32_to_bf16(o[mb][jq][2] * inv) | ((uint32_t)f32_to_bf16(o[mb][jq][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + mb * 16 + lg * 4) = w;
+      }
+    }
+  }
+}
+
+bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads) {
+  if (head_dim != PF_D || n_kv_heads <= 0 || n_heads % n_kv_heads) return false;
+  const int hpg = n_heads / n_kv_heads;
+  return hpg == 1 || hpg == 2 || hpg % 4 == 0;
+}
+
+void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0, int n_tokens,
+                         int n_heads, int n_kv_heads, int head_dim, int max_seq, void* out, hipStream_t s) {
+  if (n_tokens <= 0) return;
+  (void)head_dim;
+  const int hpg = n_heads / n_kv_heads;
+  const int hpw = hpg >= 4 ? 4 : hpg;
+  const int qb = 32 * (4 / hpw);
+  dim3 grid((n_tokens + qb - 1) / qb, n_kv_heads * (hpg / hpw));
+  const bf16_t* qq = (const bf16_t*)q;
+  const bf16_t* kk = (const bf16_t*)k_cache;
+  const bf16_t* vv = (const bf16_t*)v_cache;
+  bf16_t* oo = (bf16_t*)out;
+  if (hpw == 4)
+    attn_prefill_kernel<4><<<grid, 256, 0, s>>>(qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
+  else if (hpw == 2)
+    attn_prefill_kernel<2><<<grid, 256, 0, s>>>(qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
+  else
+    attn_prefill_kernel<1><<<grid, 256, 0, s>>>(qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
+}
+
+}  // namespace llm

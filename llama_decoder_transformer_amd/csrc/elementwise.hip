@@ -1,0 +1,206 @@
+// Embedding gather, RMSNorm, greedy argmax and small bookkeeping kernels.
+#include "common.h"
+#include "launch.h"
+
+namespace llm {
+
+// ---------------------------------------------------------------- embedding
+// Row m of the residual stream is row tok[m] of tok_embeddings, widened to fp32
+// (embedding lookup of the "Building llama3 from scratch" page).
+template <typename TW>
+__global__ void __launch_bounds__(256) embed_kernel(const TW* __restrict__ emb, const int* __restrict__ tok,
+                                                    int dim, int vocab, float* __restrict__ x, int* err) {
+  const int m = blockIdx.x;
+  const int t = tok[m];
+  float* xr = x + (size_t)m * dim;
+  if (t < 0 || t >= vocab) {
+    if (threadIdx.x == 0) atomicOr(err, 1);
+    for (int i = threadIdx.x; i < dim; i += blockDim.x) xr[i] = 0.f;
+    return;
+  }
+  const TW* er = emb + (size_t)t * dim;
+  for (int i = threadIdx.x * 4; i < dim; i += blockDim.x * 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xr[i + k] = to_f32<TW>(er[i + k]);
+  }
+}
+
+void launch_embed(int dtype, const void* emb, const int* tokens, int M, int dim, int vocab, float* x,
+                  int* err, hipStream_t s) {
+  if (M <= 0) return;
+  if (dtype == 1)
+    embed_kernel<bf16_t><<<M, 256, 0, s>>>((const bf16_t*)emb, tokens, dim, vocab, x, err);
+  else
+    embed_kernel<float><<<M, 256, 0, s>>>((const float*)emb, tokens, dim, vocab, x, err);
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// y = x / sqrt(mean(x^2) + eps) * w per row ("rms_norm" on the "Building llama3
+// from scratch" page), fp32 statistics, one rounding to the output dtype.
+template <typename TO>
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ w,
+                                                      int dim, float eps, TO* __restrict__ y) {
+  __shared__ float red[8];
+  const int m = blockIdx.x;
+  const float* xr = x + (size_t)m * dim;
+  float ss = 0.f;
+  for (int i = threadIdx.x * 4; i < dim; i += 256 * 4) {
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(xr + i);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = wave_sum(ss);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) red[wid] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tot += red[i];
+  const float inv = 1.0f / sqrtf(tot / (float)dim + eps);
+  TO* yr = y + (size_t)m * dim;
+  for (int i = threadIdx.x * 4; i < dim; i += 256 * 4) {
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(xr + i);
+    f32x4_t g = *reinterpret_cast<const f32x4_t*>(w + i);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) yr[i + k] = from_f32<TO>(v[k] * inv * g[k]);
+  }
+}
+
+void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, float eps, void* out,
+                    hipStream_t s) {
+  if (M <= 0) return;
+  if (dtype == 1)
+    rmsnorm_kernel<bf16_t><<<M, 256, 0, s>>>(x, w, dim, eps, (bf16_t*)out);
+  else
+    rmsnorm_kernel<float><<<M, 256, 0, s>>>(x, w, dim, eps, (float*)out);
+}
+
+// ---------------------------------------------------------------- small helpers
+template <typename T>
+__global__ void to_f32_kernel(const T* __restrict__ src, float* __restrict__ dst, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = to_f32<T>(src[i]);
+}
+
+void launch_to_f32(int dtype, const void* src, float* dst, size_t n, hipStream_t s) {
+  if (n == 0) return;
+  unsigned g = (unsigned)((n + 255) / 256);
+  if (dtype == 1)
+    to_f32_kernel<bf16_t><<<g, 256, 0, s>>>((const bf16_t*)src, dst, n);
+  else
+    to_f32_kernel<float><<<g, 256, 0, s>>>((const float*)src, dst, n);
+}
+
+__global__ void fill_i32_kernel(int* p, int v, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+void launch_fill_i32(int* p, int v, size_t n, hipStream_t s) {
+  if (n == 0) return;
+  fill_i32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, v, n);
+}
+
+__global__ void advance_kernel(int* positions, const int* tokens, int* out_tokens, int* step, int batch) {
+  const int b = threadIdx.x;
+  const int st = *step;
+  __syncthreads();
+  if (b < batch) {
+    positions[b] += 1;
+    out_tokens[(size_t)st * batch + b] = tokens[b];
+  }
+  if (b == 0) *step = st + 1;
+}
+
+void launch_advance(int* positions, const int* tokens, int* out_tokens, int* step_counter, int batch,
+                    hipStream_t s) {
+  advance_kernel<<<1, 1024, 0, s>>>(positions, tokens, out_tokens, step_counter, batch);
+}
+
+// ---------------------------------------------------------------- argmax
+// Token with the highest logit, lowest index on ties ("Predicción de tokens").
+// Pass 1: each block reduces ARGMAX_CHUNK entries of one row to (value, index);
+// pass 2: one wave per row reduces the block results.
+constexpr int ARGMAX_CHUNK = 4096;
+
+int argmax_blocks(int vocab) { return (vocab + ARGMAX_CHUNK - 1) / ARGMAX_CHUNK; }
+
+__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    float v = __shfl_xor(bv, o);
+    int i = __shfl_xor(bi, o);
+    better(bv, bi, v, i);
+  }
+}
+
+__global__ void __launch_bounds__(256) argmax_pass1(const float* __restrict__ logits, int vocab, int nblk,
+                                                    float* __restrict__ pv, int* __restrict__ pi) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int row = blockIdx.y, blk = blockIdx.x;
+  const float* lr = logits + (size_t)row * vocab;
+  const int lo = blk * ARGMAX_CHUNK;
+  const int hi = min(vocab, lo + ARGMAX_CHUNK);
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int i = lo + threadIdx.x; i < hi; i += 256) better(bv, bi, lr[i], i);
+  wave_argmax(bv, bi);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) { sv[wid] = bv; si[wid] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bv = sv[0]; bi = si[0];
+    for (int w = 1; w < 4; ++w) better(bv, bi, sv[w], si[w]);
+    pv[(size_t)row * nblk + blk] = bv;
+    pi[(size_t)row * nblk + blk] = bi;
+  }
+}
+
+__global__ void __launch_bounds__(64) argmax_pass2(const float* __restrict__ pv, const int* __restrict__ pi,
+                                                   int nblk, int* __restrict__ out) {
+  const int row = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int i = threadIdx.x; i < nblk; i += 64) better(bv, bi, pv[(size_t)row * nblk + i], pi[(size_t)row * nblk + i]);
+  wave_argmax(bv, bi);
+  if (threadIdx.x == 0) out[row] = bi;
+}
+
+void launch_argmax(const float* logits, int rows, int vocab, void* partial, int* out, hipStream_t s) {
+  if (rows <= 0) return;
+  const int nblk = argmax_blocks(vocab);
+  float* pv = (float*)partial;
+  int* pi = (int*)(pv + (size_t)rows * nblk);
+  argmax_pass1<<<dim3(nblk, rows), 256, 0, s>>>(logits, vocab, nblk, pv, pi);
+  argmax_pass2<<<rows, 64, 0, s>>>(pv, pi, nblk, out);
+}
+
+__global__ void __launch_bounds__(1024) argmax_rows_kernel(const float* __restrict__ logits, int vocab,
+                                                           int* __restrict__ out) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const float* lr = logits + (size_t)blockIdx.x * vocab;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int i = threadIdx.x; i < vocab; i += 1024) better(bv, bi, lr[i], i);
+  wave_argmax(bv, bi);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) { sv[wid] = bv; si[wid] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bv = sv[0]; bi = si[0];
+    for (int w = 1; w < 16; ++w) better(bv, bi, sv[w], si[w]);
+    out[blockIdx.x] = bi;
+  }
+}
+
+void launch_argmax_rows(const float* logits, int rows, int vocab, int* out, hipStream_t s) {
+  if (rows <= 0) return;
+  argmax_rows_kernel<<<rows, 1024, 0, s>>>(logits, vocab, out);
+}
+
+}  // namespace llm

@@ -1,0 +1,74 @@
+// Internal launchers of the decoder-pass kernels (host side of each .hip file).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace llm {
+
+// What a projection does with its fp32 result C[m][n] = sum_k A[m][k] * W[n][k].
+enum EpiKind : int {
+  EPI_STORE_F32 = 0,  // out_f32[m*ld + n] = C
+  EPI_RESID = 1,      // out_f32[m*ld + n] += C   (residual add into the fp32 stream)
+  EPI_QKV = 2,        // RoPE on q/k columns, q -> q_out, k/v -> KV cache
+  EPI_SWIGLU = 3      // packed rows (2c, 2c+1) = (w1 row c, w3 row c): out[m*ld + c] = silu(C0) * C1
+};
+
+struct EpiParams {
+  int kind;
+  float* out_f32;   // STORE_F32 / RESID
+  void* out_act;    // SWIGLU output or q output (activation dtype)
+  int ld;           // leading dimension of out_f32 / out_act
+  // QKV
+  void* k_cache;    // this layer's K section: [slots][G][max_seq][d]
+  void* v_cache;    // this layer's V section
+  const int* row_pos;   // device [M] positions, or null -> pos0 + m
+  const int* row_slot;  // device [M] slots, or null -> slot0
+  int pos0, slot0;
+  int n_heads, n_kv_heads, head_dim, max_seq, n_slots;
+  const float* rope_cos;  // [max_seq][head_dim/2]
+  const float* rope_sin;
+  int* err;
+};
+
+// Embedding gather: x[m][:] = float(E[tok[m]][:]).
+void launch_embed(int dtype, const void* emb, const int* tokens, int M, int dim, int vocab, float* x,
+                  int* err, hipStream_t s);
+// RMSNorm of fp32 rows into the activation dtype.
+void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, float eps, void* out,
+                    hipStream_t s);
+// Widen a [n] vector of the storage dtype to fp32.
+void launch_to_f32(int dtype, const void* src, float* dst, size_t n, hipStream_t s);
+void launch_fill_i32(int* p, int v, size_t n, hipStream_t s);
+// Greedy argmax per row (two passes through `partial`, >= rows*argmax_blocks(vocab)*2 words).
+int argmax_blocks(int vocab);
+void launch_argmax(const float* logits, int rows, int vocab, void* partial, int* out, hipStream_t s);
+// Greedy argmax per row in one pass (one 1024-thread workgroup per row, no scratch).
+void launch_argmax_rows(const float* logits, int rows, int vocab, int* out, hipStream_t s);
+// After a generation step: positions[b] += 1; out_tokens[step*B + b] = tokens[b]; step++.
+void launch_advance(int* positions, const int* tokens, int* out_tokens, int* step_counter, int batch,
+                    hipStream_t s);
+
+// Projections.
+// bf16 MFMA GEMM for M >= 16 (A bf16 [M][K], W bf16 [N][K]).
+void launch_gemm_bf16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep,
+                      hipStream_t s);
+// Vector GEMV for small M (A and W in the activation / weight dtype).
+void launch_gemv(int dtype, const void* A, const void* W, int M, int N, int K, const EpiParams& ep,
+                 hipStream_t s);
+
+// Attention.
+// Split-KV decode attention: rows with explicit (slot, pos); q [rows][H*d].
+int attn_decode_chunk(int rows, int n_kv_heads, int max_seq);
+size_t attn_decode_partial_floats(int rows, int n_heads, int head_dim, int max_seq);
+void launch_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                        const int* row_pos, const int* row_slot, int pos0, int slot0, int rows,
+                        int n_heads, int n_kv_heads, int head_dim, int max_seq, int n_slots,
+                        float* partial, void* out, int* err, hipStream_t s);
+// Causal GQA prefill attention on MFMA (bf16, head_dim 128): queries at pos0 + i for one slot.
+bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads);
+void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0,
+                         int n_tokens, int n_heads, int n_kv_heads, int head_dim, int max_seq,
+                         void* out, hipStream_t s);
+
+}  // namespace llm

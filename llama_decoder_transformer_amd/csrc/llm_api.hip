@@ -1,0 +1,523 @@
+// C ABI of the decoder pass: validation, weight packing, buffer layout and the
+// per-layer launch sequence.  Declarations and contracts live in include/llm.h.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+#include "llm.h"
+
+using namespace llm;
+
+namespace {
+
+thread_local std::string g_err;
+
+llm_status fail(llm_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t elem_size(const llm_config& c) { return c.dtype == LLM_BF16 ? 2 : 4; }
+
+bool config_ok(const llm_config* c, std::string* why) {
+  auto bad = [&](const char* m) { if (why) *why = m; return false; };
+  if (!c) return bad("config is NULL");
+  if (c->dim <= 0 || c->n_layers <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->vocab_size <= 0 ||
+      c->max_seq_len <= 0 || c->ffn_hidden_dim <= 0)
+    return bad("every size must be positive");
+  if (c->dtype != LLM_F32 && c->dtype != LLM_BF16) return bad("dtype must be LLM_F32 or LLM_BF16");
+  if (c->max_batch < 1 || c->max_batch > 1024) return bad("max_batch must be in [1, 1024]");
+  if (c->max_prefill_tokens < 1) return bad("max_prefill_tokens must be >= 1");
+  if (c->dim % c->n_heads) return bad("dim must be a multiple of n_heads");
+  if (c->n_heads % c->n_kv_heads) return bad("n_heads must be a multiple of n_kv_heads");
+  const int hd = c->dim / c->n_heads;
+  if (hd != 48 && hd != 64 && hd != 128) return bad("head_dim must be 48, 64 or 128");
+  const int hpg = c->n_heads / c->n_kv_heads;
+  if (hpg > 4 && hpg % 4) return bad("n_heads / n_kv_heads must be <= 4 or a multiple of 4");
+  if (c->dim % 8 || c->ffn_hidden_dim % 8) return bad("dim and ffn_hidden_dim must be multiples of 8");
+  if (!(c->rope_theta > 0.f) || !(c->norm_eps >= 0.f)) return bad("rope_theta must be > 0 and norm_eps >= 0");
+  if ((long long)c->max_seq_len * c->max_batch > (1LL << 31)) return bad("max_seq_len * max_batch too large");
+  return true;
+}
+
+struct Dims {
+  int dim, L, H, G, hd, F, V, S, B, P;
+  size_t es;
+  explicit Dims(const llm_config& c)
+      : dim(c.dim), L(c.n_layers), H(c.n_heads), G(c.n_kv_heads), hd(c.dim / c.n_heads), F(c.ffn_hidden_dim),
+        V(c.vocab_size), S(c.max_seq_len), B(c.max_batch), P(c.max_prefill_tokens), es(elem_size(c)) {}
+  int qkv_rows() const { return (H + 2 * G) * hd; }
+  int rows() const { return P > B ? P : B; }
+};
+
+// Packed-weight layout.
+struct PackedLayout {
+  size_t emb, out, norm, cos, sin, layer0, layer_stride;
+  size_t l_attn_norm, l_ffn_norm, l_wqkv, l_wo, l_w13, l_w2;
+  size_t total;
+  explicit PackedLayout(const llm_config& c) {
+    Dims d(c);
+    size_t o = 0;
+    emb = o; o = align256(o + (size_t)d.V * d.dim * d.es);
+    out = o; o = align256(o + (size_t)d.V * d.dim * d.es);
+    norm = o; o = align256(o + (size_t)d.dim * 4);
+    cos = o; o = align256(o + (size_t)d.S * (d.hd / 2) * 4);
+    sin = o; o = align256(o + (size_t)d.S * (d.hd / 2) * 4);
+    layer0 = o;
+    size_t p = 0;
+    l_attn_norm = p; p = align256(p + (size_t)d.dim * 4);
+    l_ffn_norm = p; p = align256(p + (size_t)d.dim * 4);
+    l_wqkv = p; p = align256(p + (size_t)d.qkv_rows() * d.dim * d.es);
+    l_wo = p; p = align256(p + (size_t)d.dim * d.H * d.hd * d.es);
+    l_w13 = p; p = align256(p + (size_t)2 * d.F * d.dim * d.es);
+    l_w2 = p; p = align256(p + (size_t)d.dim * d.F * d.es);
+    layer_stride = p;
+    total = layer0 + (size_t)d.L * layer_stride;
+  }
+};
+
+// Workspace layout.
+struct WorkLayout {
+  size_t flags, x, a, q, o, u, attn, amax, total;
+  explicit WorkLayout(const llm_config& c) {
+    Dims d(c);
+    const size_t R = (size_t)d.rows();
+    size_t p = 0;
+    flags = p; p = align256(p + 256);
+    x = p; p = align256(p + R * d.dim * 4);
+    a = p; p = align256(p + R * d.dim * d.es);
+    q = p; p = align256(p + R * d.H * d.hd * d.es);
+    o = p; p = align256(p + R * d.H * d.hd * d.es);
+    u = p; p = align256(p + R * d.F * d.es);
+    const bool mfma_prefill = c.dtype == LLM_BF16 && attn_prefill_supported(d.hd, d.H, d.G);
+    const int att_rows = mfma_prefill ? d.B : d.rows();
+    attn = p; p = align256(p + attn_decode_partial_floats(att_rows, d.H, d.hd, d.S) * 4);
+    amax = p; p = align256(p + (size_t)d.B * argmax_blocks(d.V) * 8);
+    total = p;
+  }
+};
+
+size_t kv_bytes(const llm_config& c) {
+  Dims d(c);
+  return (size_t)d.L * 2 * d.B * d.G * d.S * d.hd * d.es;
+}
+
+}  // namespace
+
+struct LayerPtrs {
+  float* attn_norm;
+  float* ffn_norm;
+  void* wqkv;
+  void* wo;
+  void* w13;
+  void* w2;
+};
+
+struct GraphEntry {
+  int batch;
+  const void* ptrs[5];
+  hipGraphExec_t exec;
+};
+
+struct llm_model {
+  llm_config cfg;
+  int hd;
+  size_t es;
+  char* packed;
+  void* emb;
+  void* out_w;
+  float* final_norm;
+  float* rope_cos;
+  float* rope_sin;
+  std::vector<LayerPtrs> layers;
+  char* kv;
+  size_t kv_half;  // bytes of one K (or V) section of one layer
+  int* flags;      // [0] error bits, [1] generation step counter
+  float* x;
+  void* a;
+  void* q;
+  void* o;
+  void* u;
+  float* attn;
+  void* amax;
+  bool mfma_prefill;
+  hipStream_t cap_stream;
+  std::vector<GraphEntry> graphs;
+};
+
+namespace {
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+void* k_section(llm_model* m, int l) { return m->kv + (size_t)(2 * l) * m->kv_half; }
+void* v_section(llm_model* m, int l) { return m->kv + (size_t)(2 * l + 1) * m->kv_half; }
+
+EpiParams base_epi(llm_model* m) {
+  EpiParams e;
+  std::memset(&e, 0, sizeof(e));
+  e.n_heads = m->cfg.n_heads;
+  e.n_kv_heads = m->cfg.n_kv_heads;
+  e.head_dim = m->hd;
+  e.max_seq = m->cfg.max_seq_len;
+  e.n_slots = m->cfg.max_batch;
+  e.rope_cos = m->rope_cos;
+  e.rope_sin = m->rope_sin;
+  e.err = m->flags;
+  return e;
+}
+
+void project(llm_model* m, const void* A, const void* W, int M, int N, int K, const EpiParams& ep, hipStream_t s) {
+  if (m->cfg.dtype == LLM_BF16 && M > 8)
+    launch_gemm_bf16(A, W, M, N, K, ep, s);
+  else
+    launch_gemv(m->cfg.dtype, A, W, M, N, K, ep, s);
+}
+
+// One decoder block on M rows of m->x.  Rows are either a prefill run
+// (row_pos == nullptr: positions pos0.., slot slot0) or decode rows with their
+// own positions and slots.
+void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_slot, int pos0, int slot0,
+               bool prefill, hipStream_t s) {
+  const llm_config& c = m->cfg;
+  const LayerPtrs& L = m->layers[l];
+  const int H = c.n_heads, G = c.n_kv_heads, hd = m->hd, dim = c.dim, F = c.ffn_hidden_dim;
+
+  launch_rmsnorm(c.dtype, m->x, L.attn_norm, M, dim, c.norm_eps, m->a, s);
+
+  EpiParams e = base_epi(m);
+  e.kind = EPI_QKV;
+  e.out_act = m->q;
+  e.ld = H * hd;
+  e.k_cache = k_section(m, l);
+  e.v_cache = v_section(m, l);
+  e.row_pos = row_pos;
+  e.row_slot = row_slot;
+  e.pos0 = pos0;
+  e.slot0 = slot0;
+  project(m, m->a, L.wqkv, M, (H + 2 * G) * hd, dim, e, s);
+
+  if (prefill && m->mfma_prefill)
+    launch_attn_prefill(m->q, k_section(m, l), v_section(m, l), slot0, pos0, M, H, G, hd, c.max_seq_len, m->o, s);
+  else
+    launch_attn_decode(c.dtype, m->q, k_section(m, l), v_section(m, l), row_pos, row_slot, pos0, slot0, M, H, G, hd,
+                       c.max_seq_len, c.max_batch, m->attn, m->o, m->flags, s);
+
+  EpiParams r = base_epi(m);
+  r.kind = EPI_RESID;
+  r.out_f32 = m->x;
+  r.ld = dim;
+  project(m, m->o, L.wo, M, dim, H * hd, r, s);
+
+  launch_rmsnorm(c.dtype, m->x, L.ffn_norm, M, dim, c.norm_eps, m->a, s);
+
+  EpiParams g = base_epi(m);
+  g.kind = EPI_SWIGLU;
+  g.out_act = m->u;
+  g.ld = F;
+  project(m, m->a, L.w13, M, 2 * F, dim, g, s);
+
+  project(m, m->u, L.w2, M, dim, F, r, s);
+}
+
+llm_status hip_check(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(LLM_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return LLM_OK;
+}
+
+// Final RMSNorm of `rows` rows starting at x_row0, then the output projection.
+void lm_head(llm_model* m, const float* x_rows, int rows, float* logits, hipStream_t s) {
+  const llm_config& c = m->cfg;
+  launch_rmsnorm(c.dtype, x_rows, m->final_norm, rows, c.dim, c.norm_eps, m->a, s);
+  EpiParams e = base_epi(m);
+  e.kind = EPI_STORE_F32;
+  e.out_f32 = logits;
+  e.ld = c.vocab_size;
+  project(m, m->a, m->out_w, rows, c.vocab_size, c.dim, e, s);
+}
+
+void enqueue_decode(llm_model* m, int batch, const int* slots, const int* positions, const int* tokens, float* logits,
+                    hipStream_t s) {
+  const llm_config& c = m->cfg;
+  launch_embed(c.dtype, m->emb, tokens, batch, c.dim, c.vocab_size, m->x, m->flags, s);
+  for (int l = 0; l < c.n_layers; ++l) run_layer(m, l, batch, positions, slots, 0, 0, false, s);
+  lm_head(m, m->x, batch, logits, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+llm_status llm_check_config(const llm_config* cfg) {
+  std::string why;
+  if (!config_ok(cfg, &why)) return fail(LLM_ERR_CONFIG, why);
+  return LLM_OK;
+}
+
+size_t llm_packed_weight_bytes(const llm_config* cfg) {
+  if (!config_ok(cfg, nullptr)) return 0;
+  return PackedLayout(*cfg).total;
+}
+
+size_t llm_kv_cache_bytes(const llm_config* cfg) {
+  if (!config_ok(cfg, nullptr)) return 0;
+  return kv_bytes(*cfg);
+}
+
+size_t llm_workspace_bytes(const llm_config* cfg) {
+  if (!config_ok(cfg, nullptr)) return 0;
+  return WorkLayout(*cfg).total;
+}
+
+llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* packed, size_t packed_bytes,
+                            void* kv_cache, size_t kv_cache_bytes, void* workspace, size_t workspace_bytes,
+                            void* stream, llm_model** out) {
+  if (!out) return fail(LLM_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  std::string why;
+  if (!config_ok(cfg, &why)) return fail(LLM_ERR_CONFIG, why);
+  if (!w || !packed || !kv_cache || !workspace) return fail(LLM_ERR_INVALID_ARG, "weights or a buffer is NULL");
+  const llm_config& c = *cfg;
+  Dims d(c);
+  if (!w->tok_embeddings || !w->norm || !w->output || !w->attention_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+      !w->ffn_norm || !w->w1 || !w->w3 || !w->w2)
+    return fail(LLM_ERR_INVALID_ARG, "a weight pointer is NULL");
+  for (int l = 0; l < d.L; ++l)
+    if (!w->attention_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->w1[l] ||
+        !w->w3[l] || !w->w2[l])
+      return fail(LLM_ERR_INVALID_ARG, "layer " + std::to_string(l) + " has a NULL weight pointer");
+  PackedLayout pl(c);
+  WorkLayout wl(c);
+  if (packed_bytes < pl.total) return fail(LLM_ERR_BUFFER_TOO_SMALL, "packed weight buffer too small");
+  if (kv_cache_bytes < kv_bytes(c)) return fail(LLM_ERR_BUFFER_TOO_SMALL, "KV cache buffer too small");
+  if (workspace_bytes < wl.total) return fail(LLM_ERR_BUFFER_TOO_SMALL, "workspace buffer too small");
+
+  hipStream_t s = as_stream(stream);
+  llm_model* m = new llm_model();
+  m->cfg = c;
+  m->hd = d.hd;
+  m->es = d.es;
+  m->packed = (char*)packed;
+  m->emb = m->packed + pl.emb;
+  m->out_w = m->packed + pl.out;
+  m->final_norm = (float*)(m->packed + pl.norm);
+  m->rope_cos = (float*)(m->packed + pl.cos);
+  m->rope_sin = (float*)(m->packed + pl.sin);
+  m->layers.resize(d.L);
+  m->kv = (char*)kv_cache;
+  m->kv_half = (size_t)d.B * d.G * d.S * d.hd * d.es;
+  char* ws = (char*)workspace;
+  m->flags = (int*)(ws + wl.flags);
+  m->x = (float*)(ws + wl.x);
+  m->a = ws + wl.a;
+  m->q = ws + wl.q;
+  m->o = ws + wl.o;
+  m->u = ws + wl.u;
+  m->attn = (float*)(ws + wl.attn);
+  m->amax = ws + wl.amax;
+  m->mfma_prefill = c.dtype == LLM_BF16 && attn_prefill_supported(d.hd, d.H, d.G);
+  m->cap_stream = nullptr;
+
+  const size_t es = d.es;
+  const size_t row = (size_t)d.dim * es;
+  hipError_t e = hipSuccess;
+  auto cp = [&](void* dst, const void* src, size_t n) {
+    if (e == hipSuccess) e = hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, s);
+  };
+  cp(m->emb, w->tok_embeddings, (size_t)d.V * row);
+  cp(m->out_w, w->output, (size_t)d.V * row);
+  launch_to_f32(c.dtype, w->norm, m->final_norm, d.dim, s);
+  for (int l = 0; l < d.L; ++l) {
+    char* base = m->packed + pl.layer0 + (size_t)l * pl.layer_stride;
+    LayerPtrs& L = m->layers[l];
+    L.attn_norm = (float*)(base + pl.l_attn_norm);
+    L.ffn_norm = (float*)(base + pl.l_ffn_norm);
+    L.wqkv = base + pl.l_wqkv;
+    L.wo = base + pl.l_wo;
+    L.w13 = base + pl.l_w13;
+    L.w2 = base + pl.l_w2;
+    launch_to_f32(c.dtype, w->attention_norm[l], L.attn_norm, d.dim, s);
+    launch_to_f32(c.dtype, w->ffn_norm[l], L.ffn_norm, d.dim, s);
+    // q|k|v rows concatenated.
+    cp(L.wqkv, w->wq[l], (size_t)d.H * d.hd * row);
+    cp((char*)L.wqkv + (size_t)d.H * d.hd * row, w->wk[l], (size_t)d.G * d.hd * row);
+    cp((char*)L.wqkv + (size_t)(d.H + d.G) * d.hd * row, w->wv[l], (size_t)d.G * d.hd * row);
+    cp(L.wo, w->wo[l], (size_t)d.dim * d.H * d.hd * es);
+    // w1 / w3 rows interleaved: packed row 2c = w1 row c, 2c + 1 = w3 row c.
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(L.w13, 2 * row, w->w1[l], row, row, d.F, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync((char*)L.w13 + row, 2 * row, w->w3[l], row, row, d.F, hipMemcpyDeviceToDevice, s);
+    cp(L.w2, w->w2[l], (size_t)d.dim * d.F * es);
+  }
+  // RoPE tables: angle(pos, j) = pos * theta^(-2j/hd) in fp64, stored as fp32 cos / sin.
+  const int half = d.hd / 2;
+  std::vector<float> hc((size_t)d.S * half), hs((size_t)d.S * half);
+  for (int j = 0; j < half; ++j) {
+    const double f = std::pow((double)c.rope_theta, -2.0 * j / (double)d.hd);
+    for (int p = 0; p < d.S; ++p) {
+      const double a = (double)p * f;
+      hc[(size_t)p * half + j] = (float)std::cos(a);
+      hs[(size_t)p * half + j] = (float)std::sin(a);
+    }
+  }
+  if (e == hipSuccess) e = hipMemcpyAsync(m->rope_cos, hc.data(), hc.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(m->rope_sin, hs.data(), hs.size() * 4, hipMemcpyHostToDevice, s);
+  launch_fill_i32(m->flags, 0, 64, s);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    delete m;
+    return fail(LLM_ERR_HIP, std::string("init: ") + hipGetErrorString(e));
+  }
+  *out = m;
+  return LLM_OK;
+}
+
+llm_status llm_prefill(llm_model* m, int32_t slot, const int32_t* tokens_dev, int32_t n_tokens, int32_t start_pos,
+                       float* logits_dev, void* stream) {
+  if (!m || !tokens_dev || !logits_dev) return fail(LLM_ERR_INVALID_ARG, "NULL model, tokens or logits");
+  const llm_config& c = m->cfg;
+  if (n_tokens < 1) return fail(LLM_ERR_INVALID_ARG, "n_tokens must be >= 1");
+  if (n_tokens > c.max_prefill_tokens) return fail(LLM_ERR_OUT_OF_RANGE, "n_tokens > max_prefill_tokens");
+  if (slot < 0 || slot >= c.max_batch) return fail(LLM_ERR_OUT_OF_RANGE, "slot out of range");
+  if (start_pos < 0 || (long long)start_pos + n_tokens > c.max_seq_len)
+    return fail(LLM_ERR_OUT_OF_RANGE, "start_pos + n_tokens > max_seq_len");
+  hipStream_t s = as_stream(stream);
+  launch_embed(c.dtype, m->emb, tokens_dev, n_tokens, c.dim, c.vocab_size, m->x, m->flags, s);
+  for (int l = 0; l < c.n_layers; ++l) run_layer(m, l, n_tokens, nullptr, nullptr, start_pos, slot, true, s);
+  lm_head(m, m->x + (size_t)(n_tokens - 1) * c.dim, 1, logits_dev, s);
+  return hip_check("prefill launch");
+}
+
+llm_status llm_layer_forward(llm_model* m, int32_t layer, int32_t slot, float* x_dev, int32_t n_tokens,
+                             int32_t start_pos, void* stream) {
+  if (!m || !x_dev) return fail(LLM_ERR_INVALID_ARG, "NULL model or x");
+  const llm_config& c = m->cfg;
+  if (layer < 0 || layer >= c.n_layers) return fail(LLM_ERR_OUT_OF_RANGE, "layer out of range");
+  if (n_tokens < 1) return fail(LLM_ERR_INVALID_ARG, "n_tokens must be >= 1");
+  if (n_tokens > c.max_prefill_tokens) return fail(LLM_ERR_OUT_OF_RANGE, "n_tokens > max_prefill_tokens");
+  if (slot < 0 || slot >= c.max_batch) return fail(LLM_ERR_OUT_OF_RANGE, "slot out of range");
+  if (start_pos < 0 || (long long)start_pos + n_tokens > c.max_seq_len)
+    return fail(LLM_ERR_OUT_OF_RANGE, "start_pos + n_tokens > max_seq_len");
+  hipStream_t s = as_stream(stream);
+  hipError_t e = hipMemcpyAsync(m->x, x_dev, (size_t)n_tokens * c.dim * 4, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return fail(LLM_ERR_HIP, hipGetErrorString(e));
+  run_layer(m, layer, n_tokens, nullptr, nullptr, start_pos, slot, true, s);
+  e = hipMemcpyAsync(x_dev, m->x, (size_t)n_tokens * c.dim * 4, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return fail(LLM_ERR_HIP, hipGetErrorString(e));
+  return hip_check("layer launch");
+}
+
+llm_status llm_decode_step(llm_model* m, int32_t batch, const int32_t* slots_dev, const int32_t* positions_dev,
+                           const int32_t* tokens_dev, float* logits_dev, void* stream) {
+  if (!m || !slots_dev || !positions_dev || !tokens_dev || !logits_dev)
+    return fail(LLM_ERR_INVALID_ARG, "NULL model or buffer");
+  if (batch < 1) return fail(LLM_ERR_INVALID_ARG, "batch must be >= 1");
+  if (batch > m->cfg.max_batch) return fail(LLM_ERR_OUT_OF_RANGE, "batch > max_batch");
+  enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, as_stream(stream));
+  return hip_check("decode launch");
+}
+
+llm_status llm_argmax(const float* logits_dev, int32_t rows, int32_t vocab, int32_t* out_dev, void* stream) {
+  if (!logits_dev || !out_dev) return fail(LLM_ERR_INVALID_ARG, "NULL logits or out");
+  if (rows < 1 || vocab < 1) return fail(LLM_ERR_INVALID_ARG, "rows and vocab must be >= 1");
+  launch_argmax_rows(logits_dev, rows, vocab, out_dev, as_stream(stream));
+  return hip_check("argmax launch");
+}
+
+llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev, int32_t* positions_dev,
+                        int32_t* tokens_dev, int32_t n_steps, int32_t* out_tokens_dev, float* logits_dev,
+                        void* stream) {
+  if (!m || !slots_dev || !positions_dev || !tokens_dev || !out_tokens_dev || !logits_dev)
+    return fail(LLM_ERR_INVALID_ARG, "NULL model or buffer");
+  if (batch < 1 || n_steps < 0) return fail(LLM_ERR_INVALID_ARG, "batch must be >= 1 and n_steps >= 0");
+  if (batch > m->cfg.max_batch) return fail(LLM_ERR_OUT_OF_RANGE, "batch > max_batch");
+  hipStream_t s = as_stream(stream);
+  if (n_steps == 0) return LLM_OK;
+  int* step = m->flags + 1;
+  launch_fill_i32(step, 0, 1, s);
+
+  const void* key[5] = {slots_dev, positions_dev, tokens_dev, out_tokens_dev, logits_dev};
+  hipGraphExec_t exec = nullptr;
+  for (auto& g : m->graphs)
+    if (g.batch == batch && !std::memcmp(g.ptrs, key, sizeof(key))) exec = g.exec;
+  if (!exec) {
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed);
+    if (e == hipSuccess) {
+      enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, m->cap_stream);
+      launch_argmax(logits_dev, batch, m->cfg.vocab_size, m->amax, tokens_dev, m->cap_stream);
+      launch_advance(positions_dev, tokens_dev, out_tokens_dev, step, batch, m->cap_stream);
+      e = hipStreamEndCapture(m->cap_stream, &graph);
+    }
+    if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (graph) (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      exec = nullptr;
+    } else {
+      if (m->graphs.size() >= 8) {
+        (void)hipGraphExecDestroy(m->graphs.front().exec);
+        m->graphs.erase(m->graphs.begin());
+      }
+      GraphEntry ge;
+      ge.batch = batch;
+      std::memcpy(ge.ptrs, key, sizeof(key));
+      ge.exec = exec;
+      m->graphs.push_back(ge);
+    }
+  }
+  for (int i = 0; i < n_steps; ++i) {
+    if (exec) {
+      hipError_t e = hipGraphLaunch(exec, s);
+      if (e != hipSuccess) return fail(LLM_ERR_HIP, std::string("graph launch: ") + hipGetErrorString(e));
+    } else {
+      enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, s);
+      launch_argmax(logits_dev, batch, m->cfg.vocab_size, m->amax, tokens_dev, s);
+      launch_advance(positions_dev, tokens_dev, out_tokens_dev, step, batch, s);
+    }
+  }
+  return hip_check("generate launch");
+}
+
+llm_status llm_read_device_error(llm_model* m, int32_t* flags, void* stream) {
+  if (!m || !flags) return fail(LLM_ERR_INVALID_ARG, "NULL model or flags");
+  hipStream_t s = as_stream(stream);
+  int host = 0;
+  hipError_t e = hipMemcpyAsync(&host, m->flags, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(LLM_ERR_HIP, hipGetErrorString(e));
+  launch_fill_i32(m->flags, 0, 1, s);
+  *flags = host;
+  return hip_check("clear device error");
+}
+
+void llm_free(llm_model* m) {
+  if (!m) return;
+  for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  delete m;
+}
+
+const char* llm_status_string(llm_status s) {
+  switch (s) {
+    case LLM_OK: return "ok";
+    case LLM_ERR_INVALID_ARG: return "invalid argument";
+    case LLM_ERR_CONFIG: return "invalid configuration";
+    case LLM_ERR_OUT_OF_RANGE: return "out of range";
+    case LLM_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case LLM_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* llm_last_error_message(void) { return g_err.c_str(); }
+
+}  // extern "C"
