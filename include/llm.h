@@ -203,6 +203,21 @@ llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev,
  * (LLM_DEVERR_* bits) in *flags.  Errors: INVALID_ARG, HIP. */
 llm_status llm_read_device_error(llm_model* m, int32_t* flags, void* stream);
 
+/*
+ * Kernel timing (diagnostics).  While enabled, each kernel group the library
+ * launches directly on a stream is bracketed by two hipEvents recorded on that
+ * stream (llm_generate then launches directly instead of replaying its graph).
+ * Enabling resets the totals.  llm_kernel_timing synchronises on the recorded
+ * events and returns, for one LLM_K_* group, the number of bracketed launches
+ * and their summed duration in milliseconds.  Errors: INVALID_ARG, HIP.
+ */
+enum {
+  LLM_K_EMBED = 0, LLM_K_RMSNORM = 1, LLM_K_QKV = 2, LLM_K_ATTN = 3, LLM_K_WO = 4,
+  LLM_K_GATE_UP = 5, LLM_K_DOWN = 6, LLM_K_LM_HEAD = 7, LLM_K_ARGMAX = 8, LLM_K_COUNT = 9
+};
+llm_status llm_set_kernel_timing(llm_model* m, int32_t enable);
+llm_status llm_kernel_timing(llm_model* m, int32_t kind, int64_t* launches, double* total_ms);
+
 /* Release the host-side handle (no device memory is freed). NULL is allowed. */
 void llm_free(llm_model* m);
 

@@ -27,8 +27,9 @@ DEVERR_TOKEN, DEVERR_POSITION, DEVERR_SLOT = 1, 2, 4
 
 EXPORTED = ("llm_check_config", "llm_packed_weight_bytes", "llm_kv_cache_bytes", "llm_workspace_bytes",
             "llm_init_weights", "llm_prefill", "llm_layer_forward", "llm_decode_step", "llm_argmax",
-            "llm_generate", "llm_read_device_error", "llm_free", "llm_status_string",
-            "llm_last_error_message")
+            "llm_generate", "llm_read_device_error", "llm_set_kernel_timing", "llm_kernel_timing",
+            "llm_free", "llm_status_string", "llm_last_error_message")
+KERNEL_GROUPS = ("embed", "rmsnorm", "qkv", "attn", "wo", "gate_up", "down", "lm_head", "argmax")
 
 
 class LibraryMissing(RuntimeError):
@@ -82,6 +83,8 @@ def lib():
             "llm_generate": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                        c_void_p, c_void_p]),
             "llm_read_device_error": (c_int32, [c_void_p, POINTER(c_int32), c_void_p]),
+            "llm_set_kernel_timing": (c_int32, [c_void_p, c_int32]),
+            "llm_kernel_timing": (c_int32, [c_void_p, c_int32, POINTER(ctypes.c_int64), POINTER(ctypes.c_double)]),
             "llm_free": (None, [c_void_p]),
             "llm_status_string": (c_char_p, [c_int32]),
             "llm_last_error_message": (c_char_p, []),
@@ -166,6 +169,17 @@ def llm_read_device_error(handle: int, stream=None) -> int:
     f = c_int32(0)
     _check(lib().llm_read_device_error(handle, ctypes.byref(f), _stream(stream)))
     return f.value
+
+
+def llm_set_kernel_timing(handle: int, enable: bool) -> None:
+    _check(lib().llm_set_kernel_timing(handle, 1 if enable else 0))
+
+
+def llm_kernel_timing(handle: int, kind: int) -> tuple[int, float]:
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib().llm_kernel_timing(handle, kind, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
 
 
 def llm_free(handle: int) -> None:

@@ -148,11 +148,65 @@ struct llm_model {
   bool mfma_prefill;
   hipStream_t cap_stream;
   std::vector<GraphEntry> graphs;
+  // kernel timing (llm_set_kernel_timing)
+  bool timing = false;
+  struct Bracket { int kind; hipEvent_t a, b; };
+  std::vector<Bracket> pending;
+  std::vector<hipEvent_t> event_pool;
+  int64_t t_launches[LLM_K_COUNT] = {};
+  double t_ms[LLM_K_COUNT] = {};
 };
 
 namespace {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+hipEvent_t take_event(llm_model* m) {
+  if (!m->event_pool.empty()) {
+    hipEvent_t e = m->event_pool.back();
+    m->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets the launches made during its lifetime with two events when timing is on.
+struct Timed {
+  llm_model* m;
+  int kind;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  Timed(llm_model* m_, int kind_, hipStream_t s_) : m(m_), kind(kind_), s(s_) {
+    if (m->timing && (a = take_event(m))) (void)hipEventRecord(a, s);
+  }
+  ~Timed() {
+    if (!a) return;
+    hipEvent_t b = take_event(m);
+    if (!b) return;
+    (void)hipEventRecord(b, s);
+    m->pending.push_back({kind, a, b});
+  }
+};
+
+llm_status resolve_timing(llm_model* m) {
+  for (auto& br : m->pending) {
+    hipError_t e = hipEventSynchronize(br.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, br.a, br.b);
+    if (e != hipSuccess) {
+      m->pending.clear();
+      return LLM_ERR_HIP;
+    }
+    m->t_launches[br.kind] += 1;
+    m->t_ms[br.kind] += ms;
+    m->event_pool.push_back(br.a);
+    m->event_pool.push_back(br.b);
+  }
+  m->pending.clear();
+  return LLM_OK;
+}
 
 void* k_section(llm_model* m, int l) { return m->kv + (size_t)(2 * l) * m->kv_half; }
 void* v_section(llm_model* m, int l) { return m->kv + (size_t)(2 * l + 1) * m->kv_half; }
@@ -187,7 +241,10 @@ void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   const LayerPtrs& L = m->layers[l];
   const int H = c.n_heads, G = c.n_kv_heads, hd = m->hd, dim = c.dim, F = c.ffn_hidden_dim;
 
-  launch_rmsnorm(c.dtype, m->x, L.attn_norm, M, dim, c.norm_eps, m->a, s);
+  {
+    Timed t(m, LLM_K_RMSNORM, s);
+    launch_rmsnorm(c.dtype, m->x, L.attn_norm, M, dim, c.norm_eps, m->a, s);
+  }
 
   EpiParams e = base_epi(m);
   e.kind = EPI_QKV;
@@ -199,29 +256,47 @@ void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   e.row_slot = row_slot;
   e.pos0 = pos0;
   e.slot0 = slot0;
-  project(m, m->a, L.wqkv, M, (H + 2 * G) * hd, dim, e, s);
+  {
+    Timed t(m, LLM_K_QKV, s);
+    project(m, m->a, L.wqkv, M, (H + 2 * G) * hd, dim, e, s);
+  }
 
-  if (prefill && m->mfma_prefill)
-    launch_attn_prefill(m->q, k_section(m, l), v_section(m, l), slot0, pos0, M, H, G, hd, c.max_seq_len, m->o, s);
-  else
-    launch_attn_decode(c.dtype, m->q, k_section(m, l), v_section(m, l), row_pos, row_slot, pos0, slot0, M, H, G, hd,
-                       c.max_seq_len, c.max_batch, m->attn, m->o, m->flags, s);
+  {
+    Timed t(m, LLM_K_ATTN, s);
+    if (prefill && m->mfma_prefill)
+      launch_attn_prefill(m->q, k_section(m, l), v_section(m, l), slot0, pos0, M, H, G, hd, c.max_seq_len, m->o, s);
+    else
+      launch_attn_decode(c.dtype, m->q, k_section(m, l), v_section(m, l), row_pos, row_slot, pos0, slot0, M, H, G,
+                         hd, c.max_seq_len, c.max_batch, m->attn, m->o, m->flags, s);
+  }
 
   EpiParams r = base_epi(m);
   r.kind = EPI_RESID;
   r.out_f32 = m->x;
   r.ld = dim;
-  project(m, m->o, L.wo, M, dim, H * hd, r, s);
+  {
+    Timed t(m, LLM_K_WO, s);
+    project(m, m->o, L.wo, M, dim, H * hd, r, s);
+  }
 
-  launch_rmsnorm(c.dtype, m->x, L.ffn_norm, M, dim, c.norm_eps, m->a, s);
+  {
+    Timed t(m, LLM_K_RMSNORM, s);
+    launch_rmsnorm(c.dtype, m->x, L.ffn_norm, M, dim, c.norm_eps, m->a, s);
+  }
 
   EpiParams g = base_epi(m);
   g.kind = EPI_SWIGLU;
   g.out_act = m->u;
   g.ld = F;
-  project(m, m->a, L.w13, M, 2 * F, dim, g, s);
+  {
+    Timed t(m, LLM_K_GATE_UP, s);
+    project(m, m->a, L.w13, M, 2 * F, dim, g, s);
+  }
 
-  project(m, m->u, L.w2, M, dim, F, r, s);
+  {
+    Timed t(m, LLM_K_DOWN, s);
+    project(m, m->u, L.w2, M, dim, F, r, s);
+  }
 }
 
 llm_status hip_check(const char* what) {
@@ -233,7 +308,11 @@ llm_status hip_check(const char* what) {
 // Final RMSNorm of `rows` rows starting at x_row0, then the output projection.
 void lm_head(llm_model* m, const float* x_rows, int rows, float* logits, hipStream_t s) {
   const llm_config& c = m->cfg;
-  launch_rmsnorm(c.dtype, x_rows, m->final_norm, rows, c.dim, c.norm_eps, m->a, s);
+  {
+    Timed t(m, LLM_K_RMSNORM, s);
+    launch_rmsnorm(c.dtype, x_rows, m->final_norm, rows, c.dim, c.norm_eps, m->a, s);
+  }
+  Timed t(m, LLM_K_LM_HEAD, s);
   EpiParams e = base_epi(m);
   e.kind = EPI_STORE_F32;
   e.out_f32 = logits;
@@ -244,7 +323,10 @@ void lm_head(llm_model* m, const float* x_rows, int rows, float* logits, hipStre
 void enqueue_decode(llm_model* m, int batch, const int* slots, const int* positions, const int* tokens, float* logits,
                     hipStream_t s) {
   const llm_config& c = m->cfg;
-  launch_embed(c.dtype, m->emb, tokens, batch, c.dim, c.vocab_size, m->x, m->flags, s);
+  {
+    Timed t(m, LLM_K_EMBED, s);
+    launch_embed(c.dtype, m->emb, tokens, batch, c.dim, c.vocab_size, m->x, m->flags, s);
+  }
   for (int l = 0; l < c.n_layers; ++l) run_layer(m, l, batch, positions, slots, 0, 0, false, s);
   lm_head(m, m->x, batch, logits, s);
 }
@@ -390,7 +472,10 @@ llm_status llm_prefill(llm_model* m, int32_t slot, const int32_t* tokens_dev, in
   if (start_pos < 0 || (long long)start_pos + n_tokens > c.max_seq_len)
     return fail(LLM_ERR_OUT_OF_RANGE, "start_pos + n_tokens > max_seq_len");
   hipStream_t s = as_stream(stream);
-  launch_embed(c.dtype, m->emb, tokens_dev, n_tokens, c.dim, c.vocab_size, m->x, m->flags, s);
+  {
+    Timed t(m, LLM_K_EMBED, s);
+    launch_embed(c.dtype, m->emb, tokens_dev, n_tokens, c.dim, c.vocab_size, m->x, m->flags, s);
+  }
   for (int l = 0; l < c.n_layers; ++l) run_layer(m, l, n_tokens, nullptr, nullptr, start_pos, slot, true, s);
   lm_head(m, m->x + (size_t)(n_tokens - 1) * c.dim, 1, logits_dev, s);
   return hip_check("prefill launch");
@@ -446,9 +531,10 @@ llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev, i
 
   const void* key[5] = {slots_dev, positions_dev, tokens_dev, out_tokens_dev, logits_dev};
   hipGraphExec_t exec = nullptr;
-  for (auto& g : m->graphs)
-    if (g.batch == batch && !std::memcmp(g.ptrs, key, sizeof(key))) exec = g.exec;
-  if (!exec) {
+  if (!m->timing)
+    for (auto& g : m->graphs)
+      if (g.batch == batch && !std::memcmp(g.ptrs, key, sizeof(key))) exec = g.exec;
+  if (!exec && !m->timing) {
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed);
     if (e == hipSuccess) {
@@ -480,6 +566,7 @@ llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev, i
       if (e != hipSuccess) return fail(LLM_ERR_HIP, std::string("graph launch: ") + hipGetErrorString(e));
     } else {
       enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, s);
+      Timed t(m, LLM_K_ARGMAX, s);
       launch_argmax(logits_dev, batch, m->cfg.vocab_size, m->amax, tokens_dev, s);
       launch_advance(positions_dev, tokens_dev, out_tokens_dev, step, batch, s);
     }
@@ -499,8 +586,27 @@ llm_status llm_read_device_error(llm_model* m, int32_t* flags, void* stream) {
   return hip_check("clear device error");
 }
 
+llm_status llm_set_kernel_timing(llm_model* m, int32_t enable) {
+  if (!m) return fail(LLM_ERR_INVALID_ARG, "NULL model");
+  if (resolve_timing(m) != LLM_OK) return fail(LLM_ERR_HIP, "timing events failed");
+  m->timing = enable != 0;
+  for (int k = 0; k < LLM_K_COUNT; ++k) { m->t_launches[k] = 0; m->t_ms[k] = 0.0; }
+  return LLM_OK;
+}
+
+llm_status llm_kernel_timing(llm_model* m, int32_t kind, int64_t* launches, double* total_ms) {
+  if (!m || !launches || !total_ms) return fail(LLM_ERR_INVALID_ARG, "NULL model or output");
+  if (kind < 0 || kind >= LLM_K_COUNT) return fail(LLM_ERR_INVALID_ARG, "unknown kernel group");
+  if (resolve_timing(m) != LLM_OK) return fail(LLM_ERR_HIP, "timing events failed");
+  *launches = m->t_launches[kind];
+  *total_ms = m->t_ms[kind];
+  return LLM_OK;
+}
+
 void llm_free(llm_model* m) {
   if (!m) return;
+  (void)resolve_timing(m);
+  for (auto e : m->event_pool) (void)hipEventDestroy(e);
   for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   delete m;
