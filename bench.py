@@ -193,7 +193,7 @@ def main() -> int:
     L, dim, F, V = shape.n_layers, shape.dim, shape.ffn_hidden_dim, shape.vocab_size
     n_up, ms_up = kt_decode["gate_up"]
     up_avg_ms = ms_up / n_up
-    up_bytes = 2 * F * dim * 2 + dim * 2 + F * 2  # w1|w3 weights + normed row in + SwiGLU row out
+    up_bytes = 2 * F * dim * 2 + 2 * dim * 4 + F * 2  # w1|w3 weights + fp32 x and norm weight in + SwiGLU row out
     up_gbs = up_bytes / (up_avg_ms * 1e-3) / 1e9
     n_pup, ms_pup = kt_prefill["gate_up"]
     pup_avg_ms = ms_pup / n_pup

@@ -20,10 +20,15 @@ constexpr float LOG2E_F = 1.4426950408889634f;
 //
 // Grid (chunk, kv-head x head-block, row).  A workgroup handles one row (decode
 // sequence or prefill token), one KV head, up to 4 of its query heads, and the
-// CH keys of one chunk; 16 groups of 16 lanes each take one key at a time, a
-// lane holding d/16 elements (16 bytes for bf16 d = 128).  Each group keeps its
-// own running max / sum / accumulator; the 16 groups are merged through LDS and
-// written as a partial (max, sum, acc[d]) that attn_combine merges over chunks.
+// CH keys of one chunk.  16 groups of 16 lanes each take 4 keys per round of 64
+// (all 8 K/V loads of a round are issued before any arithmetic), a lane holding
+// d/16 elements (16 bytes for bf16 d = 128).  Each group keeps its own running
+// max / sum / accumulator; the groups are merged through LDS.  A row whose keys
+// fit one chunk is written out directly; otherwise each chunk writes a partial
+// (max, sum, acc[d]) that attn_combine_kernel merges.  (Merging in the last
+// workgroup to arrive needs agent-scope fences, which cost more than the extra
+// launch on this GPU.)  Short caches with few rows use one 1024-thread
+// workgroup per (row, query head) and no merge pass at all.
 
 constexpr int DEC_MAXH = 4;
 
@@ -37,80 +42,113 @@ __device__ __forceinline__ void load_epl(const T* p, float* out) {
   }
 }
 
-template <typename T, int D>
-__global__ void __launch_bounds__(256) attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc,
-                                                          const T* __restrict__ vc, const int* __restrict__ row_pos,
-                                                          const int* __restrict__ row_slot, int pos0, int slot0,
-                                                          int H, int G, int max_seq, int n_slots, int CH, int nchunks,
-                                                          int hpb, float* __restrict__ partial) {
+template <typename T, int D, int NT, int MAXH>
+__global__ void __launch_bounds__(NT) attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc,
+                                                         const T* __restrict__ vc, const int* __restrict__ row_pos,
+                                                         const int* __restrict__ row_slot, int pos0, int slot0,
+                                                         int H, int G, int max_seq, int n_slots, int CH, int nchunks,
+                                                         int hpb, float* partial, T* __restrict__ out, int* err) {
   constexpr int EPL = D / 16;
-  __shared__ float s_m[16][DEC_MAXH];
-  __shared__ float s_l[16][DEC_MAXH];
-  __shared__ float s_acc[16][DEC_MAXH][D];
+  constexpr int NG = NT / 16;  // groups of 16 lanes
+  __shared__ float s_m[NG][MAXH];
+  __shared__ float s_l[NG][MAXH];
+  __shared__ float s_acc[NG][MAXH][D];
 
   const int chunk = blockIdx.x, gy = blockIdx.y, row = blockIdx.z;
   const int hpg = H / G;
   const int nhb = hpg / hpb;
   const int g = gy / nhb;
   const int h0 = g * hpg + (gy % nhb) * hpb;
+  const int tid = threadIdx.x, grp = tid >> 4, gl = tid & 15;
   const int pos = row_pos ? row_pos[row] : pos0 + row;
   const int slot = row_slot ? row_slot[row] : slot0;
-  if (pos < 0 || pos >= max_seq || slot < 0 || slot >= n_slots) return;
+  T* orow = out + (size_t)row * H * D;
+  if (pos < 0 || pos >= max_seq || slot < 0 || slot >= n_slots) {
+    if (chunk == 0) {
+      for (int t = tid; t < hpb * D; t += NT) orow[(size_t)h0 * D + t] = from_f32<T>(0.f);
+      if (tid == 0) atomicOr(err, (pos < 0 || pos >= max_seq) ? 2 : 4);
+    }
+    return;
+  }
   const int start = chunk * CH;
   if (start > pos) return;
   const int end = min(pos + 1, start + CH);
-
-  const int tid = threadIdx.x, grp = tid >> 4, gl = tid & 15;
+  const int nvalid = pos / CH + 1;
   const float scale = LOG2E_F / sqrtf((float)D);
 
-  float qv[DEC_MAXH][EPL];
+  const size_t base = ((size_t)slot * G + g) * (size_t)max_seq * D;
+  const T* kb = kc + base;
+  const T* vb = vc + base;
+
+  float qv[MAXH][EPL];
 #pragma unroll
-  for (int hh = 0; hh < DEC_MAXH; ++hh) {
+  for (int hh = 0; hh < MAXH; ++hh) {
     if (hh < hpb) {
       load_epl<T, EPL>(q + (size_t)row * H * D + (size_t)(h0 + hh) * D + gl * EPL, qv[hh]);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) qv[hh][e] *= scale;
     }
   }
-  float mx[DEC_MAXH], sm[DEC_MAXH], acc[DEC_MAXH][EPL];
+  float mx[MAXH], sm[MAXH], acc[MAXH][EPL];
 #pragma unroll
-  for (int hh = 0; hh < DEC_MAXH; ++hh) {
+  for (int hh = 0; hh < MAXH; ++hh) {
     mx[hh] = -1e30f;
     sm[hh] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
   }
 
-  const size_t base = ((size_t)slot * G + g) * (size_t)max_seq * D;
-  const T* kb = kc + base;
-  const T* vb = vc + base;
-  for (int j = start + grp; j < end; j += 16) {
-    float kv[EPL], vv[EPL];
-    load_epl<T, EPL>(kb + (size_t)j * D + gl * EPL, kv);
-    load_epl<T, EPL>(vb + (size_t)j * D + gl * EPL, vv);
+  for (int r0 = start; r0 < end; r0 += 4 * NG) {
+    float kv[4][EPL], vv[4][EPL];
+    bool ok[4];
 #pragma unroll
-    for (int hh = 0; hh < DEC_MAXH; ++hh) {
+    for (int t = 0; t < 4; ++t) {
+      const int j = r0 + grp + NG * t;
+      ok[t] = j < end;
+      if (ok[t]) {
+        load_epl<T, EPL>(kb + (size_t)j * D + gl * EPL, kv[t]);
+        load_epl<T, EPL>(vb + (size_t)j * D + gl * EPL, vv[t]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) { kv[t][e] = 0.f; vv[t][e] = 0.f; }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < MAXH; ++hh) {
       if (hh < hpb) {
-        float s = 0.f;
+        float sc[4];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s = fmaf(qv[hh][e], kv[e], s);
-        s += __shfl_xor(s, 8);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 1);
-        const float mn = fmaxf(mx[hh], s);
+        for (int t = 0; t < 4; ++t) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) d = fmaf(qv[hh][e], kv[t][e], d);
+          d += __shfl_xor(d, 8);
+          d += __shfl_xor(d, 4);
+          d += __shfl_xor(d, 2);
+          d += __shfl_xor(d, 1);
+          sc[t] = ok[t] ? d : -INFINITY;
+        }
+        const float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        const float mn = fmaxf(mx[hh], mloc);
         const float alpha = exp2f(mx[hh] - mn);
-        const float p = exp2f(s - mn);
-        sm[hh] = sm[hh] * alpha + p;
+        float p[4];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(p, vv[e], acc[hh][e] * alpha);
+        for (int t = 0; t < 4; ++t) p[t] = exp2f(sc[t] - mn);
+        sm[hh] = sm[hh] * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float a = acc[hh][e] * alpha;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) a = fmaf(p[t], vv[t][e], a);
+          acc[hh][e] = a;
+        }
         mx[hh] = mn;
       }
     }
   }
 
 #pragma unroll
-  for (int hh = 0; hh < DEC_MAXH; ++hh) {
+  for (int hh = 0; hh < MAXH; ++hh) {
     if (hh < hpb) {
       if (gl == 0) { s_m[grp][hh] = mx[hh]; s_l[grp][hh] = sm[hh]; }
 #pragma unroll
@@ -118,48 +156,67 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(const T* __restrict__ 
     }
   }
   __syncthreads();
-  for (int t = tid; t < hpb * D; t += 256) {
+  for (int t = tid; t < hpb * D; t += NT) {
     const int hh = t / D, e = t % D;
     float M = -1e30f;
-    for (int i = 0; i < 16; ++i) M = fmaxf(M, s_m[i][hh]);
+    for (int i = 0; i < NG; ++i) M = fmaxf(M, s_m[i][hh]);
     float L = 0.f, a = 0.f;
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NG; ++i) {
       const float w = exp2f(s_m[i][hh] - M);
       L += s_l[i][hh] * w;
       a += s_acc[i][hh][e] * w;
     }
-    float* pr = partial + (((size_t)row * H + h0 + hh) * nchunks + chunk) * (D + 2);
-    pr[e] = a;
-    if (e == 0) { pr[D] = M; pr[D + 1] = L; }
+    if (nvalid == 1) {
+      orow[(size_t)(h0 + hh) * D + e] = from_f32<T>(a / L);
+    } else {
+      float* pr = partial + (((size_t)row * H + h0 + hh) * nchunks + chunk) * (D + 2);
+      pr[e] = a;
+      if (e == 0) { pr[D] = M; pr[D + 1] = L; }
+    }
   }
 }
 
-// Merge the chunk partials of one (row, head): o = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M).
+// Merge the chunk partials of one (row, head) when the row spans several chunks:
+// o = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M), M = max_c m_c.
 template <typename T, int D>
-__global__ void attn_combine_kernel(const float* __restrict__ partial, const int* __restrict__ row_pos,
-                                    const int* __restrict__ row_slot, int pos0, int slot0, int H, int max_seq,
-                                    int n_slots, int CH, int nchunks, T* __restrict__ out, int* err) {
-  const int h = blockIdx.x, row = blockIdx.y, e = threadIdx.x;
+__global__ void __launch_bounds__(128) attn_combine_kernel(const float* __restrict__ partial,
+                                                           const int* __restrict__ row_pos,
+                                                           const int* __restrict__ row_slot, int pos0, int slot0,
+                                                           int H, int max_seq, int n_slots, int CH, int nchunks,
+                                                           T* __restrict__ out) {
+  const int h = blockIdx.x, row = blockIdx.y;
   const int pos = row_pos ? row_pos[row] : pos0 + row;
   const int slot = row_slot ? row_slot[row] : slot0;
-  T* o = out + (size_t)row * H * D + (size_t)h * D;
-  if (pos < 0 || pos >= max_seq || slot < 0 || slot >= n_slots) {
-    if (e < D) o[e] = from_f32<T>(0.f);
-    if (e == 0 && h == 0) atomicOr(err, pos < 0 || pos >= max_seq ? 2 : 4);
-    return;
-  }
+  if (pos < 0 || pos >= max_seq || slot < 0 || slot >= n_slots) return;
   const int nv = pos / CH + 1;
+  if (nv == 1) return;
   const float* pr = partial + ((size_t)row * H + h) * nchunks * (D + 2);
-  float M = -1e30f;
-  for (int c = 0; c < nv; ++c) M = fmaxf(M, pr[(size_t)c * (D + 2) + D]);
-  float L = 0.f, a = 0.f;
-  for (int c = 0; c < nv; ++c) {
-    const float* pc = pr + (size_t)c * (D + 2);
-    const float w = exp2f(pc[D] - M);
-    L += pc[D + 1] * w;
-    if (e < D) a += pc[e] * w;
+  extern __shared__ float s_w[];  // [nchunks] chunk weights
+  __shared__ float s_inv;
+  // chunk weights 2^(m_c - M) and 1 / L, computed by the first wave
+  if (threadIdx.x < 64) {
+    float mc = -1e30f, lc = 0.f;
+    for (int c = threadIdx.x; c < nv; c += 64) {
+      mc = fmaxf(mc, pr[(size_t)c * (D + 2) + D]);
+    }
+    const float M = wave_max(mc);
+    float L = 0.f;
+    for (int c = threadIdx.x; c < nv; c += 64) {
+      const float w = exp2f(pr[(size_t)c * (D + 2) + D] - M);
+      lc = pr[(size_t)c * (D + 2) + D + 1];
+      s_w[c] = w;
+      L += w * lc;
+    }
+    L = wave_sum(L);
+    if (threadIdx.x == 0) s_inv = 1.0f / L;
   }
-  if (e < D) o[e] = from_f32<T>(a / L);
+  __syncthreads();
+  for (int e = threadIdx.x; e < D; e += 128) {
+    float a = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < nv; ++c) a += pr[(size_t)c * (D + 2) + e] * s_w[c];
+    out[(size_t)row * H * D + (size_t)h * D + e] = from_f32<T>(a * s_inv);
+  }
 }
 
 int attn_decode_chunk(int rows, int n_kv_heads, int max_seq) {
@@ -173,19 +230,37 @@ size_t attn_decode_partial_floats(int rows, int n_heads, int head_dim, int max_s
   return (size_t)rows * n_heads * nch * (head_dim + 2);
 }
 
+static int dec_hpb(int n_heads, int n_kv_heads) {
+  const int hpg = n_heads / n_kv_heads;
+  return hpg <= DEC_MAXH ? hpg : DEC_MAXH;
+}
+
+// One chunk per row (no merge pass) when the cache is short and there are few rows:
+// 1024-thread workgroups, one query head each.
+static bool dec_single_pass(int rows, int n_heads, int max_seq) {
+  return max_seq <= 1024 && rows * n_heads <= 512;
+}
+
 template <typename T, int D>
 static void attn_decode_dispatch(const T* q, const T* kc, const T* vc, const int* row_pos, const int* row_slot,
                                  int pos0, int slot0, int rows, int H, int G, int max_seq, int n_slots,
                                  float* partial, T* out, int* err, hipStream_t s) {
+  const int hpg = H / G;
+  if (dec_single_pass(rows, H, max_seq)) {
+    dim3 grid(1, H, rows);
+    attn_decode_kernel<T, D, 1024, 1><<<grid, 1024, 0, s>>>(q, kc, vc, row_pos, row_slot, pos0, slot0, H, G, max_seq,
+                                                           n_slots, max_seq, 1, 1, partial, out, err);
+    return;
+  }
   const int CH = attn_decode_chunk(rows, G, max_seq);
   const int nch = (max_seq + CH - 1) / CH;
-  const int hpg = H / G;
-  const int hpb = hpg <= DEC_MAXH ? hpg : DEC_MAXH;
+  const int hpb = dec_hpb(H, G);
   dim3 grid(nch, G * (hpg / hpb), rows);
-  attn_decode_kernel<T, D><<<grid, 256, 0, s>>>(q, kc, vc, row_pos, row_slot, pos0, slot0, H, G, max_seq, n_slots,
-                                               CH, nch, hpb, partial);
-  attn_combine_kernel<T, D><<<dim3(H, rows), D < 64 ? 64 : D, 0, s>>>(partial, row_pos, row_slot, pos0, slot0, H,
-                                                                      max_seq, n_slots, CH, nch, out, err);
+  attn_decode_kernel<T, D, 256, DEC_MAXH><<<grid, 256, 0, s>>>(q, kc, vc, row_pos, row_slot, pos0, slot0, H, G,
+                                                              max_seq, n_slots, CH, nch, hpb, partial, out, err);
+  if (nch > 1)
+    attn_combine_kernel<T, D><<<dim3(H, rows), 128, nch * sizeof(float), s>>>(partial, row_pos, row_slot, pos0, slot0,
+                                                                            H, max_seq, n_slots, CH, nch, out);
 }
 
 void launch_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache, const int* row_pos,

@@ -1,112 +1,309 @@
 // Small-M projections (decode steps, tiny prefills): y[m][n] = sum_k a[m][k] * W[n][k].
 //
-// Batch-1 decode is bound by streaming the weight matrix from HBM once, so each
-// wave owns RPW consecutive weight rows and walks K with 16-byte loads per lane
-// (a wave reads 1 KiB of one row per load instruction), keeping RPW * UNROLL
-// loads in flight.  The activations (at most MR rows) are re-read from L1/L2.
-// Partial sums are reduced across the wave with xor shuffles; the epilogue
-// (RoPE / cache write, SwiGLU, residual add, fp32 store) is applied by one lane
-// per output.
+// Batch-1 decode is bound by streaming each weight matrix from HBM once.  A
+// 256-thread block owns R consecutive weight rows; its 4 waves split K into
+// 512-element chunks taken round-robin, each lane loading 16 bytes of every row
+// per chunk (a wave reads 1 KiB of a row per load instruction).  Two chunks are
+// in flight at a time, so 2 * R loads per lane are outstanding.  Partial sums are reduced
+// across the wave with xor shuffles and across the 4 waves through LDS, and the
+// epilogue (RoPE / cache write, SwiGLU, residual add, fp32 store) runs on the
+// R * MR finished values.
+//
+// With NORM the input is the fp32 residual stream x and the RMSNorm is fused:
+// the block accumulates sum_k W[n][k] * (x[k] * g[k]) and sum_k x[k]^2 in the
+// same pass and scales by 1 / sqrt(mean(x^2) + eps) at the end (the "rms_norm"
+// of the "Building llama3 from scratch" page, distributed over the dot product).
 #include "common.h"
 #include "epilogue.h"
 #include "launch.h"
 
 namespace llm {
 
-template <typename T, int MR, int RPW, int EPI>
-__global__ void __launch_bounds__(256) gemv_kernel(const T* __restrict__ A, const T* __restrict__ W, int M,
-                                                   int N, int K, EpiParams ep) {
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int n0 = wave * RPW;
-  if (n0 >= N) return;
+template <typename T, int MR, int R, int EPI, bool NORM>
+__global__ void __launch_bounds__(256) gemv_kernel(const void* __restrict__ Ain, const T* __restrict__ W,
+                                                   const float* __restrict__ gnorm, float eps, int M, int N, int K,
+                                                   EpiParams ep) {
+  constexpr int KW = WAVE * 8;
+  __shared__ float s_acc[4][MR][R];
+  __shared__ float s_ss[4][MR];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * R;
   const int m0 = blockIdx.y * MR;
   const int mrows = min(MR, M - m0);
 
-  const T* wr[RPW];
+  const T* wr[R];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) wr[r] = W + (size_t)min(n0 + r, N - 1) * K;
+  for (int r = 0; r < R; ++r) wr[r] = W + (size_t)min(n0 + r, N - 1) * K;
 
-  float acc[MR][RPW];
+  float acc[MR][R];
+  float ss[MR];
 #pragma unroll
-  for (int i = 0; i < MR; ++i)
+  for (int i = 0; i < MR; ++i) {
+    ss[i] = 0.f;
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) acc[i][r] = 0.f;
+    for (int r = 0; r < R; ++r) acc[i][r] = 0.f;
+  }
 
+  const int nchunks = (K + KW - 1) / KW;
 #pragma unroll 2
-  for (int k = lane * 8; k < K; k += WAVE * 8) {
-    float w[RPW][8];
+  for (int c = wid; c < nchunks; c += 4) {
+    const int k = c * KW + lane * 8;
+    if (k < K) {
+      float w[R][8];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) load8(wr[r] + k, w[r]);
+      for (int r = 0; r < R; ++r) load8(wr[r] + k, w[r]);
+      float g[8];
+      if (NORM) load8(gnorm + k, g);
 #pragma unroll
-    for (int i = 0; i < MR; ++i) {
-      if (i < mrows) {
-        float a[8];
-        load8(A + (size_t)(m0 + i) * K + k, a);
+      for (int i = 0; i < MR; ++i) {
+        if (i < mrows) {
+          float a[8];
+          if (NORM) {
+            load8(reinterpret_cast<const float*>(Ain) + (size_t)(m0 + i) * K + k, a);
 #pragma unroll
-        for (int r = 0; r < RPW; ++r)
+            for (int e = 0; e < 8; ++e) {
+              ss[i] = fmaf(a[e], a[e], ss[i]);
+              a[e] *= g[e];
+            }
+          } else {
+            load8(reinterpret_cast<const T*>(Ain) + (size_t)(m0 + i) * K + k, a);
+          }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i][r] = fmaf(a[e], w[r][e], acc[i][r]);
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[i][r] = fmaf(a[e], w[r][e], acc[i][r]);
+        }
       }
     }
   }
 
 #pragma unroll
-  for (int i = 0; i < MR; ++i)
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) acc[i][r] = wave_sum(acc[i][r]);
-
-#pragma unroll
   for (int i = 0; i < MR; ++i) {
-    if (i >= mrows) break;
-    const int m = m0 + i;
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int n = n0 + r;
-      if (lane != (i * RPW + r) % WAVE || n >= N) continue;
-      const float v = acc[i][r];
+    for (int r = 0; r < R; ++r) acc[i][r] = wave_sum(acc[i][r]);
+    if (NORM) ss[i] = wave_sum(ss[i]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) s_acc[wid][i][r] = acc[i][r];
+      s_ss[wid][i] = ss[i];
+    }
+  }
+  __syncthreads();
+
+  const int t = threadIdx.x;
+  if (t < MR * R) {
+    const int i = t / R, r = t % R;
+    const int m = m0 + i, n = n0 + r;
+    if (i < mrows && n < N) {
+      float v = s_acc[0][i][r] + s_acc[1][i][r] + s_acc[2][i][r] + s_acc[3][i][r];
+      float vp = s_acc[0][i][r ^ 1] + s_acc[1][i][r ^ 1] + s_acc[2][i][r ^ 1] + s_acc[3][i][r ^ 1];
+      if (NORM) {
+        const float tot = s_ss[0][i] + s_ss[1][i] + s_ss[2][i] + s_ss[3][i];
+        const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+        v *= inv;
+        vp *= inv;
+      }
       if (EPI == EPI_STORE_F32) {
         ep.out_f32[(size_t)m * ep.ld + n] = v;
       } else if (EPI == EPI_RESID) {
         ep.out_f32[(size_t)m * ep.ld + n] += v;
       } else if (EPI == EPI_QKV) {
-        epi_qkv<T>(ep, m, n, v, acc[i][r ^ 1]);
+        epi_qkv<T>(ep, m, n, v, vp);
       } else if (EPI == EPI_SWIGLU) {
-        if ((r & 1) == 0) epi_swiglu<T>(ep, m, n >> 1, v, acc[i][r + 1]);
+        if ((r & 1) == 0) epi_swiglu<T>(ep, m, n >> 1, v, vp);
       }
     }
   }
 }
 
-template <typename T, int MR, int RPW>
-static void gemv_dispatch(const T* A, const T* W, int M, int N, int K, const EpiParams& ep, hipStream_t s) {
-  const int waves = (N + RPW - 1) / RPW;
-  dim3 grid((waves + 3) / 4, (M + MR - 1) / MR);
-  switch (ep.kind) {
-    case EPI_STORE_F32: gemv_kernel<T, MR, RPW, EPI_STORE_F32><<<grid, 256, 0, s>>>(A, W, M, N, K, ep); break;
-    case EPI_RESID: gemv_kernel<T, MR, RPW, EPI_RESID><<<grid, 256, 0, s>>>(A, W, M, N, K, ep); break;
-    case EPI_QKV: gemv_kernel<T, MR, RPW, EPI_QKV><<<grid, 256, 0, s>>>(A, W, M, N, K, ep); break;
-    case EPI_SWIGLU: gemv_kernel<T, MR, RPW, EPI_SWIGLU><<<grid, 256, 0, s>>>(A, W, M, N, K, ep); break;
+// bf16 weights: the same scheme with the weights kept as raw 16-byte words until
+// use, so two chunks x R rows of loads (2R per lane) are issued before any math.
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4_t raw, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(raw[i] << 16);
+    out[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
   }
 }
 
-void launch_gemv(int dtype, const void* A, const void* W, int M, int N, int K, const EpiParams& ep,
-                 hipStream_t s) {
+template <int MR, int R, int EPI, bool NORM>
+__global__ void __launch_bounds__(256) gemv_bf16_kernel(const void* __restrict__ Ain, const bf16_t* __restrict__ W,
+                                                        const float* __restrict__ gnorm, float eps, int M, int N,
+                                                        int K, EpiParams ep) {
+  constexpr int KW = WAVE * 8;
+  __shared__ float s_acc[4][MR][R];
+  __shared__ float s_ss[4][MR];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * R;
+  const int m0 = blockIdx.y * MR;
+  const int mrows = min(MR, M - m0);
+
+  const bf16_t* wr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wr[r] = W + (size_t)min(n0 + r, N - 1) * K;
+
+  float acc[MR][R];
+  float ss[MR];
+#pragma unroll
+  for (int i = 0; i < MR; ++i) {
+    ss[i] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[i][r] = 0.f;
+  }
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+  const int nchunks = (K + KW - 1) / KW;
+  for (int c0 = wid; c0 < nchunks; c0 += 8) {
+    int kk[2];
+    bool ok[2];
+    u32x4_t wraw[2][R];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      kk[u] = (c0 + 4 * u) * KW + lane * 8;
+      ok[u] = kk[u] < K;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        wraw[u][r] = ok[u] ? *reinterpret_cast<const u32x4_t*>(wr[r] + kk[u]) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!ok[u]) continue;
+      float g[8];
+      if (NORM) load8(gnorm + kk[u], g);
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        if (i < mrows) {
+          float a[8];
+          if (NORM) {
+            load8(reinterpret_cast<const float*>(Ain) + (size_t)(m0 + i) * K + kk[u], a);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              ss[i] = fmaf(a[e], a[e], ss[i]);
+              a[e] *= g[e];
+            }
+          } else {
+            load8(reinterpret_cast<const bf16_t*>(Ain) + (size_t)(m0 + i) * K + kk[u], a);
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            float w[8];
+            bf16x8_to_f32(wraw[u][r], w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[i][r] = fmaf(a[e], w[e], acc[i][r]);
+          }
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < MR; ++i) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[i][r] = wave_sum(acc[i][r]);
+    if (NORM) ss[i] = wave_sum(ss[i]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) s_acc[wid][i][r] = acc[i][r];
+      s_ss[wid][i] = ss[i];
+    }
+  }
+  __syncthreads();
+
+  const int t = threadIdx.x;
+  if (t < MR * R) {
+    const int i = t / R, r = t % R;
+    const int m = m0 + i, n = n0 + r;
+    if (i < mrows && n < N) {
+      float v = s_acc[0][i][r] + s_acc[1][i][r] + s_acc[2][i][r] + s_acc[3][i][r];
+      float vp = s_acc[0][i][r ^ 1] + s_acc[1][i][r ^ 1] + s_acc[2][i][r ^ 1] + s_acc[3][i][r ^ 1];
+      if (NORM) {
+        const float tot = s_ss[0][i] + s_ss[1][i] + s_ss[2][i] + s_ss[3][i];
+        const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+        v *= inv;
+        vp *= inv;
+      }
+      if (EPI == EPI_STORE_F32) {
+        ep.out_f32[(size_t)m * ep.ld + n] = v;
+      } else if (EPI == EPI_RESID) {
+        ep.out_f32[(size_t)m * ep.ld + n] += v;
+      } else if (EPI == EPI_QKV) {
+        epi_qkv<bf16_t>(ep, m, n, v, vp);
+      } else if (EPI == EPI_SWIGLU) {
+        if ((r & 1) == 0) epi_swiglu<bf16_t>(ep, m, n >> 1, v, vp);
+      }
+    }
+  }
+}
+
+template <int MR, int R, bool NORM>
+static void gemv_bf16_dispatch(const void* A, const bf16_t* W, const float* g, float eps, int M, int N, int K,
+                               const EpiParams& ep, hipStream_t s) {
+  dim3 grid((N + R - 1) / R, (M + MR - 1) / MR);
+  switch (ep.kind) {
+    case EPI_STORE_F32:
+      gemv_bf16_kernel<MR, R, EPI_STORE_F32, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep);
+      break;
+    case EPI_RESID: gemv_bf16_kernel<MR, R, EPI_RESID, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+    case EPI_QKV: gemv_bf16_kernel<MR, R, EPI_QKV, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+    case EPI_SWIGLU: gemv_bf16_kernel<MR, R, EPI_SWIGLU, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+  }
+}
+
+template <typename T, int MR, int R, bool NORM>
+static void gemv_dispatch(const void* A, const T* W, const float* g, float eps, int M, int N, int K,
+                          const EpiParams& ep, hipStream_t s) {
+  dim3 grid((N + R - 1) / R, (M + MR - 1) / MR);
+  switch (ep.kind) {
+    case EPI_STORE_F32:
+      gemv_kernel<T, MR, R, EPI_STORE_F32, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep);
+      break;
+    case EPI_RESID: gemv_kernel<T, MR, R, EPI_RESID, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+    case EPI_QKV: gemv_kernel<T, MR, R, EPI_QKV, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+    case EPI_SWIGLU: gemv_kernel<T, MR, R, EPI_SWIGLU, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+  }
+}
+
+template <bool NORM>
+static void gemv_bf16_pick(const void* A, const bf16_t* W, const float* g, float eps, int M, int N, int K,
+                           const EpiParams& ep, hipStream_t s) {
+  // Rows per block for M = 1, from a sweep of the Llama-3-8B projection shapes on MI355X:
+  // LM head (N >= 64K) 16, gate-up (N >= 16K) 8, long-K down projection 2, q|k|v 8, wo 2.
+  if (M == 1) {
+    if (N >= 65536) gemv_bf16_dispatch<1, 16, NORM>(A, W, g, eps, M, N, K, ep, s);
+    else if (N >= 16384) gemv_bf16_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s);
+    else if (K >= 8192) gemv_bf16_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+    else if (N >= 6144) gemv_bf16_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s);
+    else gemv_bf16_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+  } else if (M <= 4) {
+    gemv_bf16_dispatch<4, 4, NORM>(A, W, g, eps, M, N, K, ep, s);
+  } else {
+    gemv_bf16_dispatch<8, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+  }
+}
+
+template <bool NORM>
+static void gemv_f32_pick(const void* A, const float* W, const float* g, float eps, int M, int N, int K,
+                          const EpiParams& ep, hipStream_t s) {
+  if (M == 1) gemv_dispatch<float, 1, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+  else if (M <= 4) gemv_dispatch<float, 4, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+  else gemv_dispatch<float, 8, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+}
+
+void launch_gemv(int dtype, const void* A, const void* W, const float* norm_w, float eps, int M, int N, int K,
+                 const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
   if (dtype == 1) {
-    if (M == 1)
-      gemv_dispatch<bf16_t, 1, 4>((const bf16_t*)A, (const bf16_t*)W, M, N, K, ep, s);
-    else if (M <= 4)
-      gemv_dispatch<bf16_t, 4, 4>((const bf16_t*)A, (const bf16_t*)W, M, N, K, ep, s);
-    else
-      gemv_dispatch<bf16_t, 8, 2>((const bf16_t*)A, (const bf16_t*)W, M, N, K, ep, s);
+    if (norm_w) gemv_bf16_pick<true>(A, (const bf16_t*)W, norm_w, eps, M, N, K, ep, s);
+    else gemv_bf16_pick<false>(A, (const bf16_t*)W, nullptr, eps, M, N, K, ep, s);
   } else {
-    if (M == 1)
-      gemv_dispatch<float, 1, 4>((const float*)A, (const float*)W, M, N, K, ep, s);
-    else if (M <= 4)
-      gemv_dispatch<float, 4, 4>((const float*)A, (const float*)W, M, N, K, ep, s);
-    else
-      gemv_dispatch<float, 8, 2>((const float*)A, (const float*)W, M, N, K, ep, s);
+    if (norm_w) gemv_f32_pick<true>(A, (const float*)W, norm_w, eps, M, N, K, ep, s);
+    else gemv_f32_pick<false>(A, (const float*)W, nullptr, eps, M, N, K, ep, s);
   }
 }
 

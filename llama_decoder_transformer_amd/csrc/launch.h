@@ -53,12 +53,14 @@ void launch_advance(int* positions, const int* tokens, int* out_tokens, int* ste
 // bf16 MFMA GEMM for M >= 16 (A bf16 [M][K], W bf16 [N][K]).
 void launch_gemm_bf16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep,
                       hipStream_t s);
-// Vector GEMV for small M (A and W in the activation / weight dtype).
-void launch_gemv(int dtype, const void* A, const void* W, int M, int N, int K, const EpiParams& ep,
-                 hipStream_t s);
+// Vector GEMV for small M.  With norm_w == nullptr, A has the activation dtype; otherwise A
+// is the fp32 residual stream and the RMSNorm (weight norm_w, eps) is fused into the pass.
+void launch_gemv(int dtype, const void* A, const void* W, const float* norm_w, float eps, int M, int N, int K,
+                 const EpiParams& ep, hipStream_t s);
 
 // Attention.
-// Split-KV decode attention: rows with explicit (slot, pos); q [rows][H*d].
+// Split-KV decode attention: rows with explicit (slot, pos); q [rows][H*d]; `partial` holds
+// attn_decode_partial_floats(...) floats.
 int attn_decode_chunk(int rows, int n_kv_heads, int max_seq);
 size_t attn_decode_partial_floats(int rows, int n_heads, int head_dim, int max_seq);
 void launch_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,

@@ -41,6 +41,7 @@ bool config_ok(const llm_config* c, std::string* why) {
   if (hpg > 4 && hpg % 4) return bad("n_heads / n_kv_heads must be <= 4 or a multiple of 4");
   if (c->dim % 8 || c->ffn_hidden_dim % 8) return bad("dim and ffn_hidden_dim must be multiples of 8");
   if (!(c->rope_theta > 0.f) || !(c->norm_eps >= 0.f)) return bad("rope_theta must be > 0 and norm_eps >= 0");
+  if (c->max_seq_len > (1 << 20)) return bad("max_seq_len must be <= 1048576");
   if ((long long)c->max_seq_len * c->max_batch > (1LL << 31)) return bad("max_seq_len * max_batch too large");
   return true;
 }
@@ -89,13 +90,13 @@ struct WorkLayout {
     const size_t R = (size_t)d.rows();
     size_t p = 0;
     flags = p; p = align256(p + 256);
+    const bool mfma_prefill = c.dtype == LLM_BF16 && attn_prefill_supported(d.hd, d.H, d.G);
+    const int att_rows = mfma_prefill ? d.B : d.rows();
     x = p; p = align256(p + R * d.dim * 4);
     a = p; p = align256(p + R * d.dim * d.es);
     q = p; p = align256(p + R * d.H * d.hd * d.es);
     o = p; p = align256(p + R * d.H * d.hd * d.es);
     u = p; p = align256(p + R * d.F * d.es);
-    const bool mfma_prefill = c.dtype == LLM_BF16 && attn_prefill_supported(d.hd, d.H, d.G);
-    const int att_rows = mfma_prefill ? d.B : d.rows();
     attn = p; p = align256(p + attn_decode_partial_floats(att_rows, d.H, d.hd, d.S) * 4);
     amax = p; p = align256(p + (size_t)d.B * argmax_blocks(d.V) * 8);
     total = p;
@@ -225,11 +226,23 @@ EpiParams base_epi(llm_model* m) {
   return e;
 }
 
-void project(llm_model* m, const void* A, const void* W, int M, int N, int K, const EpiParams& ep, hipStream_t s) {
-  if (m->cfg.dtype == LLM_BF16 && M > 8)
+bool use_mfma(const llm_model* m, int M) { return m->cfg.dtype == LLM_BF16 && M > 8; }
+
+// y = A W^T with epilogue `ep`.  With norm_w, A is the fp32 residual stream and the
+// projection consumes rmsnorm(A) * norm_w: fused into the GEMV, or a separate RMSNorm
+// into m->a ahead of the MFMA GEMM.
+void project(llm_model* m, const void* A, const void* W, int M, int N, int K, const EpiParams& ep, hipStream_t s,
+             const float* norm_w = nullptr) {
+  const llm_config& c = m->cfg;
+  if (use_mfma(m, M)) {
+    if (norm_w) {
+      launch_rmsnorm(c.dtype, (const float*)A, norm_w, M, K, c.norm_eps, m->a, s);
+      A = m->a;
+    }
     launch_gemm_bf16(A, W, M, N, K, ep, s);
-  else
-    launch_gemv(m->cfg.dtype, A, W, M, N, K, ep, s);
+  } else {
+    launch_gemv(c.dtype, A, W, norm_w, c.norm_eps, M, N, K, ep, s);
+  }
 }
 
 // One decoder block on M rows of m->x.  Rows are either a prefill run
@@ -240,11 +253,6 @@ void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   const llm_config& c = m->cfg;
   const LayerPtrs& L = m->layers[l];
   const int H = c.n_heads, G = c.n_kv_heads, hd = m->hd, dim = c.dim, F = c.ffn_hidden_dim;
-
-  {
-    Timed t(m, LLM_K_RMSNORM, s);
-    launch_rmsnorm(c.dtype, m->x, L.attn_norm, M, dim, c.norm_eps, m->a, s);
-  }
 
   EpiParams e = base_epi(m);
   e.kind = EPI_QKV;
@@ -258,7 +266,7 @@ void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   e.slot0 = slot0;
   {
     Timed t(m, LLM_K_QKV, s);
-    project(m, m->a, L.wqkv, M, (H + 2 * G) * hd, dim, e, s);
+    project(m, m->x, L.wqkv, M, (H + 2 * G) * hd, dim, e, s, L.attn_norm);
   }
 
   {
@@ -279,18 +287,13 @@ void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
     project(m, m->o, L.wo, M, dim, H * hd, r, s);
   }
 
-  {
-    Timed t(m, LLM_K_RMSNORM, s);
-    launch_rmsnorm(c.dtype, m->x, L.ffn_norm, M, dim, c.norm_eps, m->a, s);
-  }
-
   EpiParams g = base_epi(m);
   g.kind = EPI_SWIGLU;
   g.out_act = m->u;
   g.ld = F;
   {
     Timed t(m, LLM_K_GATE_UP, s);
-    project(m, m->a, L.w13, M, 2 * F, dim, g, s);
+    project(m, m->x, L.w13, M, 2 * F, dim, g, s, L.ffn_norm);
   }
 
   {
@@ -308,16 +311,12 @@ llm_status hip_check(const char* what) {
 // Final RMSNorm of `rows` rows starting at x_row0, then the output projection.
 void lm_head(llm_model* m, const float* x_rows, int rows, float* logits, hipStream_t s) {
   const llm_config& c = m->cfg;
-  {
-    Timed t(m, LLM_K_RMSNORM, s);
-    launch_rmsnorm(c.dtype, x_rows, m->final_norm, rows, c.dim, c.norm_eps, m->a, s);
-  }
   Timed t(m, LLM_K_LM_HEAD, s);
   EpiParams e = base_epi(m);
   e.kind = EPI_STORE_F32;
   e.out_f32 = logits;
   e.ld = c.vocab_size;
-  project(m, m->a, m->out_w, rows, c.vocab_size, c.dim, e, s);
+  project(m, x_rows, m->out_w, rows, c.vocab_size, c.dim, e, s, m->final_norm);
 }
 
 void enqueue_decode(llm_model* m, int batch, const int* slots, const int* positions, const int* tokens, float* logits,
@@ -451,6 +450,7 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   if (e == hipSuccess) e = hipMemcpyAsync(m->rope_cos, hc.data(), hc.size() * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(m->rope_sin, hs.data(), hs.size() * 4, hipMemcpyHostToDevice, s);
   launch_fill_i32(m->flags, 0, 64, s);
+
   if (e == hipSuccess) e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
