@@ -16,13 +16,20 @@ namespace llm {
 
 constexpr float LOG2E_F = 1.4426950408889634f;
 
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f16x2_t h;
+  h.x = (f16_t)a;
+  h.y = (f16_t)b;
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // ============================================================== split-KV decode
 //
 // Grid (chunk, kv-head x head-block, row).  A workgroup handles one row (decode
 // sequence or prefill token), one KV head, up to 4 of its query heads, and the
 // CH keys of one chunk.  16 groups of 16 lanes each take 4 keys per round of 64
 // (all 8 K/V loads of a round are issued before any arithmetic), a lane holding
-// d/16 elements (16 bytes for bf16 d = 128).  Each group keeps its own running
+// d/16 elements (16 bytes for fp16 d = 128).  Each group keeps its own running
 // max / sum / accumulator; the groups are merged through LDS.  A row whose keys
 // fit one chunk is written out directly; otherwise each chunk writes a partial
 // (max, sum, acc[d]) that attn_combine_kernel merges.  (Merging in the last
@@ -272,9 +279,9 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
   attn_decode_dispatch<T, D>((const T*)q, (const T*)k_cache, (const T*)v_cache, row_pos, row_slot, pos0, slot0, \
                              rows, n_heads, n_kv_heads, max_seq, n_slots, partial, (T*)out, err, s)
   if (dtype == 1) {
-    if (head_dim == 128) LLM_DEC(bf16_t, 128);
-    else if (head_dim == 64) LLM_DEC(bf16_t, 64);
-    else LLM_DEC(bf16_t, 48);
+    if (head_dim == 128) LLM_DEC(f16_t, 128);
+    else if (head_dim == 64) LLM_DEC(f16_t, 64);
+    else LLM_DEC(f16_t, 48);
   } else {
     if (head_dim == 128) LLM_DEC(float, 128);
     else if (head_dim == 64) LLM_DEC(float, 64);
@@ -285,7 +292,7 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 
 // ============================================================== MFMA prefill
 //
-// bf16, head_dim 128.  Grid (query block, kv-head x head-block).  A workgroup
+// fp16 operands, fp32 accumulation and softmax, head_dim 128.  Grid (query block, kv-head x head-block).  A workgroup
 // holds 4 waves; each wave owns 32 queries of one query head, and the waves of
 // a workgroup share one KV head so a K/V tile of 64 keys is staged in LDS once
 // for all of them (GQA packing: 4 query heads x 32 queries when the group has 4
@@ -294,7 +301,7 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 // Per 64-key tile a wave computes S^T = K Q^T (keys as MFMA rows, queries as
 // columns), so each lane's accumulators all belong to one query column: the
 // softmax max needs only two cross-lane steps and the scaled probabilities,
-// packed to bf16, are already the B operand of O^T += V^T P^T.  The k-order of
+// packed to fp16, are already the B operand of O^T += V^T P^T.  The k-order of
 // that second product is the permutation {4g..4g+3, 16+4g..16+4g+3} of each
 // 32-key slice that the first product leaves in lane group g; the V^T operand is
 // read from a transposed LDS copy of V in the same order.
@@ -305,13 +312,13 @@ constexpr int PF_KLD = PF_D + 8;   // Ks row: 272 bytes
 constexpr int PF_VLD = PF_KT + 8;  // Vt row: 144 bytes
 
 template <int HPW>
-__global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
-                                                           const bf16_t* __restrict__ vc, int slot, int pos0, int S,
-                                                           int H, int G, int max_seq, bf16_t* __restrict__ out) {
+__global__ void __launch_bounds__(256) attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc,
+                                                           const f16_t* __restrict__ vc, int slot, int pos0, int S,
+                                                           int H, int G, int max_seq, f16_t* __restrict__ out) {
   constexpr int QSUB = 4 / HPW;  // 32-query sub-blocks per workgroup
   constexpr int QB = 32 * QSUB;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[PF_KT * PF_KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[PF_D * PF_VLD];
+  __shared__ __attribute__((aligned(16))) f16_t Ks[PF_KT * PF_KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[PF_D * PF_VLD];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -327,7 +334,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restr
   const float scale = LOG2E_F / sqrtf((float)PF_D);
 
   // Q fragments (B operand): column = query jq*16 + l16, k = 32 s + 8 lg .. +7.
-  bf16x8_t qf[2][4];
+  f16x8_t qf[2][4];
 #pragma unroll
   for (int jq = 0; jq < 2; ++jq) {
     const int i = qw0 + jq * 16 + l16;
@@ -335,7 +342,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restr
     for (int s4 = 0; s4 < 4; ++s4) {
       u32x4_t raw = {0u, 0u, 0u, 0u};
       if (i < S) raw = *reinterpret_cast<const u32x4_t*>(q + (size_t)i * ld_q + head * PF_D + s4 * 32 + lg * 8);
-      qf[jq][s4] = __builtin_bit_cast(bf16x8_t, raw);
+      qf[jq][s4] = __builtin_bit_cast(f16x8_t, raw);
     }
   }
 
@@ -347,8 +354,8 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restr
   float mrow[2] = {-1e30f, -1e30f}, lrow[2] = {0.f, 0.f};
 
   const size_t base = ((size_t)slot * G + g) * (size_t)max_seq * PF_D;
-  const bf16_t* kb = kc + base;
-  const bf16_t* vb = vc + base;
+  const f16_t* kb = kc + base;
+  const f16_t* vb = vc + base;
   const int ntiles = (kv_end + PF_KT - 1) / PF_KT;
   const int wave_last_pos = pos0 + qw0 + 31;
 
@@ -371,8 +378,8 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restr
       if (k0 + key < kv_end) raw = *reinterpret_cast<const u32x4_t*>(vb + (size_t)(k0 + key) * PF_D + c * 8);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        Vt[(c * 8 + 2 * w) * PF_VLD + key] = (bf16_t)(raw[w] & 0xFFFFu);
-        Vt[(c * 8 + 2 * w + 1) * PF_VLD + key] = (bf16_t)(raw[w] >> 16);
+        Vt[(c * 8 + 2 * w) * PF_VLD + key] = (uint16_t)(raw[w] & 0xFFFFu);
+        Vt[(c * 8 + 2 * w + 1) * PF_VLD + key] = (uint16_t)(raw[w] >> 16);
       }
     }
     __syncthreads();
@@ -388,16 +395,15 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restr
     for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4) {
-        const bf16x8_t kf =
-            *reinterpret_cast<const bf16x8_t*>(&Ks[(kb4 * 16 + l16) * PF_KLD + s4 * 32 + lg * 8]);
+        const f16x8_t kf = *reinterpret_cast<const f16x8_t*>(&Ks[(kb4 * 16 + l16) * PF_KLD + s4 * 32 + lg * 8]);
 #pragma unroll
         for (int jq = 0; jq < 2; ++jq)
-          st[kb4][jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[jq][s4], st[kb4][jq], 0, 0, 0);
+          st[kb4][jq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[jq][s4], st[kb4][jq], 0, 0, 0);
       }
     }
 
     // Online softmax per query column.
-    bf16x8_t pf[2][2];  // [jq][k-step of 32 keys]
+    f16x8_t pf[2][2];  // [jq][k-step of 32 keys]
 #pragma unroll
     for (int jq = 0; jq < 2; ++jq) {
       const int qpos = pos0 + qw0 + jq * 16 + l16;
@@ -429,8 +435,8 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restr
         }
         // k-step kb4/2 holds blocks 2t (elements 0..3) and 2t+1 (elements 4..7).
         const int ks = kb4 >> 1, half = (kb4 & 1) * 2;
-        packed[ks][half] = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
-        packed[ks][half + 1] = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
+        packed[ks][half] = pack_f16x2(p[0], p[1]);
+        packed[ks][half + 1] = pack_f16x2(p[2], p[3]);
       }
       lrow[jq] = lrow[jq] * alpha + psum;
 #pragma unroll
@@ -438,7 +444,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restr
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         u32x4_t u = {packed[ks][0], packed[ks][1], packed[ks][2], packed[ks][3]};
-        pf[jq][ks] = __builtin_bit_cast(bf16x8_t, u);
+        pf[jq][ks] = __builtin_bit_cast(f16x8_t, u);
       }
     }
 
@@ -447,14 +453,14 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restr
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-        const bf16_t* vrow = &Vt[(mb * 16 + l16) * PF_VLD + ks * 32 + lg * 4];
+        const uint16_t* vrow = &Vt[(mb * 16 + l16) * PF_VLD + ks * 32 + lg * 4];
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
         u32x4_t u = {lo.x, lo.y, hi.x, hi.y};
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u);
+        const f16x8_t vf = __builtin_bit_cast(f16x8_t, u);
 #pragma unroll
         for (int jq = 0; jq < 2; ++jq)
-          o[mb][jq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[jq][ks], o[mb][jq], 0, 0, 0);
+          o[mb][jq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[jq][ks], o[mb][jq], 0, 0, 0);
       }
     }
   }
@@ -468,12 +474,12 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(const bf16_t* __restr
     const float inv = 1.0f / L;
     const int i = qw0 + jq * 16 + l16;
     if (i < S) {
-      bf16_t* orow = out + (size_t)i * ld_q + head * PF_D;
+      f16_t* orow = out + (size_t)i * ld_q + head * PF_D;
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
         uint2 w;
-        w.x = (uint32_t)f32_to_bf16(o[mb][jq][0] * inv) | ((uint32_t)f32_to_bf16(o[mb][jq][1] * inv) << 16);
-        w.y = (uint32_t)f32_to_bf16(o[mb][jq][2] * inv) | ((uint32_t)f32_to_bf16(o[mb][jq][3] * inv) << 16);
+        w.x = pack_f16x2(o[mb][jq][0] * inv, o[mb][jq][1] * inv);
+        w.y = pack_f16x2(o[mb][jq][2] * inv, o[mb][jq][3] * inv);
         *reinterpret_cast<uint2*>(orow + mb * 16 + lg * 4) = w;
       }
     }
@@ -494,10 +500,10 @@ void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache
   const int hpw = hpg >= 4 ? 4 : hpg;
   const int qb = 32 * (4 / hpw);
   dim3 grid((n_tokens + qb - 1) / qb, n_kv_heads * (hpg / hpw));
-  const bf16_t* qq = (const bf16_t*)q;
-  const bf16_t* kk = (const bf16_t*)k_cache;
-  const bf16_t* vv = (const bf16_t*)v_cache;
-  bf16_t* oo = (bf16_t*)out;
+  const f16_t* qq = (const f16_t*)q;
+  const f16_t* kk = (const f16_t*)k_cache;
+  const f16_t* vv = (const f16_t*)v_cache;
+  f16_t* oo = (f16_t*)out;
   if (hpw == 4)
     attn_prefill_kernel<4><<<grid, 256, 0, s>>>(qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
   else if (hpw == 2)

@@ -29,7 +29,7 @@ void launch_embed(int dtype, const void* emb, const int* tokens, int M, int dim,
                   int* err, hipStream_t s) {
   if (M <= 0) return;
   if (dtype == 1)
-    embed_kernel<bf16_t><<<M, 256, 0, s>>>((const bf16_t*)emb, tokens, dim, vocab, x, err);
+    embed_kernel<f16_t><<<M, 256, 0, s>>>((const f16_t*)emb, tokens, dim, vocab, x, err);
   else
     embed_kernel<float><<<M, 256, 0, s>>>((const float*)emb, tokens, dim, vocab, x, err);
 }
@@ -69,7 +69,7 @@ void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, f
                     hipStream_t s) {
   if (M <= 0) return;
   if (dtype == 1)
-    rmsnorm_kernel<bf16_t><<<M, 256, 0, s>>>(x, w, dim, eps, (bf16_t*)out);
+    rmsnorm_kernel<f16_t><<<M, 256, 0, s>>>(x, w, dim, eps, (f16_t*)out);
   else
     rmsnorm_kernel<float><<<M, 256, 0, s>>>(x, w, dim, eps, (float*)out);
 }
@@ -88,6 +88,24 @@ void launch_to_f32(int dtype, const void* src, float* dst, size_t n, hipStream_t
     to_f32_kernel<bf16_t><<<g, 256, 0, s>>>((const bf16_t*)src, dst, n);
   else
     to_f32_kernel<float><<<g, 256, 0, s>>>((const float*)src, dst, n);
+}
+
+// Weight packing for the bf16-weight path: rows of a bf16 matrix are widened and
+// stored as fp16 (round to nearest even; exact for every bf16 value whose
+// magnitude lies in fp16's normal range) at destination row r * row_mult + row_off.
+__global__ void pack_rows_kernel(const bf16_t* __restrict__ src, f16_t* __restrict__ dst, size_t rows, int cols,
+                                 int row_mult, int row_off) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * (size_t)cols) return;
+  const size_t r = i / cols, c = i % cols;
+  dst[(r * row_mult + row_off) * (size_t)cols + c] = (f16_t)bf16_to_f32(src[i]);
+}
+
+void launch_pack_rows(const void* src, void* dst, size_t rows, int cols, int row_mult, int row_off, hipStream_t s) {
+  const size_t n = rows * (size_t)cols;
+  if (n == 0) return;
+  pack_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const bf16_t*)src, (f16_t*)dst, rows, cols, row_mult,
+                                                               row_off);
 }
 
 __global__ void fill_i32_kernel(int* p, int v, size_t n) {

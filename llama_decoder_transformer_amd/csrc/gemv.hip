@@ -119,18 +119,12 @@ __global__ void __launch_bounds__(256) gemv_kernel(const void* __restrict__ Ain,
   }
 }
 
-// bf16 weights: the same scheme with the weights kept as raw 16-byte words until
-// use, so two chunks x R rows of loads (2R per lane) are issued before any math.
-__device__ __forceinline__ void bf16x8_to_f32(const u32x4_t raw, float* out) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = __uint_as_float(raw[i] << 16);
-    out[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
-  }
-}
+// fp16 weights (the bf16-weight path): the same scheme with the weights kept as
+// raw 16-byte words until use, so two chunks x R rows of loads (2R per lane) are
+// issued before any math.
 
 template <int MR, int R, int EPI, bool NORM>
-__global__ void __launch_bounds__(256) gemv_bf16_kernel(const void* __restrict__ Ain, const bf16_t* __restrict__ W,
+__global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ain, const f16_t* __restrict__ W,
                                                         const float* __restrict__ gnorm, float eps, int M, int N,
                                                         int K, EpiParams ep) {
   constexpr int KW = WAVE * 8;
@@ -141,7 +135,7 @@ __global__ void __launch_bounds__(256) gemv_bf16_kernel(const void* __restrict__
   const int m0 = blockIdx.y * MR;
   const int mrows = min(MR, M - m0);
 
-  const bf16_t* wr[R];
+  const f16_t* wr[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) wr[r] = W + (size_t)min(n0 + r, N - 1) * K;
 
@@ -185,12 +179,12 @@ __global__ void __launch_bounds__(256) gemv_bf16_kernel(const void* __restrict__
               a[e] *= g[e];
             }
           } else {
-            load8(reinterpret_cast<const bf16_t*>(Ain) + (size_t)(m0 + i) * K + kk[u], a);
+            load8(reinterpret_cast<const f16_t*>(Ain) + (size_t)(m0 + i) * K + kk[u], a);
           }
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             float w[8];
-            bf16x8_to_f32(wraw[u][r], w);
+            f16x8_to_f32(wraw[u][r], w);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[i][r] = fmaf(a[e], w[e], acc[i][r]);
           }
@@ -233,25 +227,25 @@ __global__ void __launch_bounds__(256) gemv_bf16_kernel(const void* __restrict__
       } else if (EPI == EPI_RESID) {
         ep.out_f32[(size_t)m * ep.ld + n] += v;
       } else if (EPI == EPI_QKV) {
-        epi_qkv<bf16_t>(ep, m, n, v, vp);
+        epi_qkv<f16_t>(ep, m, n, v, vp);
       } else if (EPI == EPI_SWIGLU) {
-        if ((r & 1) == 0) epi_swiglu<bf16_t>(ep, m, n >> 1, v, vp);
+        if ((r & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
       }
     }
   }
 }
 
 template <int MR, int R, bool NORM>
-static void gemv_bf16_dispatch(const void* A, const bf16_t* W, const float* g, float eps, int M, int N, int K,
+static void gemv_h_dispatch(const void* A, const f16_t* W, const float* g, float eps, int M, int N, int K,
                                const EpiParams& ep, hipStream_t s) {
   dim3 grid((N + R - 1) / R, (M + MR - 1) / MR);
   switch (ep.kind) {
     case EPI_STORE_F32:
-      gemv_bf16_kernel<MR, R, EPI_STORE_F32, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep);
+      gemv_h_kernel<MR, R, EPI_STORE_F32, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep);
       break;
-    case EPI_RESID: gemv_bf16_kernel<MR, R, EPI_RESID, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
-    case EPI_QKV: gemv_bf16_kernel<MR, R, EPI_QKV, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
-    case EPI_SWIGLU: gemv_bf16_kernel<MR, R, EPI_SWIGLU, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+    case EPI_RESID: gemv_h_kernel<MR, R, EPI_RESID, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+    case EPI_QKV: gemv_h_kernel<MR, R, EPI_QKV, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+    case EPI_SWIGLU: gemv_h_kernel<MR, R, EPI_SWIGLU, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
   }
 }
 
@@ -270,20 +264,20 @@ static void gemv_dispatch(const void* A, const T* W, const float* g, float eps, 
 }
 
 template <bool NORM>
-static void gemv_bf16_pick(const void* A, const bf16_t* W, const float* g, float eps, int M, int N, int K,
+static void gemv_h_pick(const void* A, const f16_t* W, const float* g, float eps, int M, int N, int K,
                            const EpiParams& ep, hipStream_t s) {
   // Rows per block for M = 1, from a sweep of the Llama-3-8B projection shapes on MI355X:
   // LM head (N >= 64K) 16, gate-up (N >= 16K) 8, long-K down projection 2, q|k|v 8, wo 2.
   if (M == 1) {
-    if (N >= 65536) gemv_bf16_dispatch<1, 16, NORM>(A, W, g, eps, M, N, K, ep, s);
-    else if (N >= 16384) gemv_bf16_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s);
-    else if (K >= 8192) gemv_bf16_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
-    else if (N >= 6144) gemv_bf16_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s);
-    else gemv_bf16_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+    if (N >= 65536) gemv_h_dispatch<1, 16, NORM>(A, W, g, eps, M, N, K, ep, s);
+    else if (N >= 16384) gemv_h_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s);
+    else if (K >= 8192) gemv_h_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+    else if (N >= 6144) gemv_h_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s);
+    else gemv_h_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
   } else if (M <= 4) {
-    gemv_bf16_dispatch<4, 4, NORM>(A, W, g, eps, M, N, K, ep, s);
+    gemv_h_dispatch<4, 4, NORM>(A, W, g, eps, M, N, K, ep, s);
   } else {
-    gemv_bf16_dispatch<8, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+    gemv_h_dispatch<8, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
   }
 }
 
@@ -299,8 +293,8 @@ void launch_gemv(int dtype, const void* A, const void* W, const float* norm_w, f
                  const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
   if (dtype == 1) {
-    if (norm_w) gemv_bf16_pick<true>(A, (const bf16_t*)W, norm_w, eps, M, N, K, ep, s);
-    else gemv_bf16_pick<false>(A, (const bf16_t*)W, nullptr, eps, M, N, K, ep, s);
+    if (norm_w) gemv_h_pick<true>(A, (const f16_t*)W, norm_w, eps, M, N, K, ep, s);
+    else gemv_h_pick<false>(A, (const f16_t*)W, nullptr, eps, M, N, K, ep, s);
   } else {
     if (norm_w) gemv_f32_pick<true>(A, (const float*)W, norm_w, eps, M, N, K, ep, s);
     else gemv_f32_pick<false>(A, (const float*)W, nullptr, eps, M, N, K, ep, s);

@@ -40,6 +40,8 @@ void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, f
 // Widen a [n] vector of the storage dtype to fp32.
 void launch_to_f32(int dtype, const void* src, float* dst, size_t n, hipStream_t s);
 void launch_fill_i32(int* p, int v, size_t n, hipStream_t s);
+// bf16 [rows][cols] -> fp16 rows placed at dst row r * row_mult + row_off.
+void launch_pack_rows(const void* src, void* dst, size_t rows, int cols, int row_mult, int row_off, hipStream_t s);
 // Greedy argmax per row (two passes through `partial`, >= rows*argmax_blocks(vocab)*2 words).
 int argmax_blocks(int vocab);
 void launch_argmax(const float* logits, int rows, int vocab, void* partial, int* out, hipStream_t s);
@@ -50,8 +52,8 @@ void launch_advance(int* positions, const int* tokens, int* out_tokens, int* ste
                     hipStream_t s);
 
 // Projections.
-// bf16 MFMA GEMM for M >= 16 (A bf16 [M][K], W bf16 [N][K]).
-void launch_gemm_bf16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep,
+// fp16 MFMA GEMM for M > 8 (A fp16 [M][K], W fp16 [N][K], fp32 accumulation).
+void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep,
                       hipStream_t s);
 // Vector GEMV for small M.  With norm_w == nullptr, A has the activation dtype; otherwise A
 // is the fp32 residual stream and the RMSNorm (weight norm_w, eps) is fused into the pass.
@@ -67,7 +69,7 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
                         const int* row_pos, const int* row_slot, int pos0, int slot0, int rows,
                         int n_heads, int n_kv_heads, int head_dim, int max_seq, int n_slots,
                         float* partial, void* out, int* err, hipStream_t s);
-// Causal GQA prefill attention on MFMA (bf16, head_dim 128): queries at pos0 + i for one slot.
+// Causal GQA prefill attention on MFMA (fp16, head_dim 128): queries at pos0 + i for one slot.
 bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads);
 void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0,
                          int n_tokens, int n_heads, int n_kv_heads, int head_dim, int max_seq,

@@ -239,7 +239,7 @@ void project(llm_model* m, const void* A, const void* W, int M, int N, int K, co
       launch_rmsnorm(c.dtype, (const float*)A, norm_w, M, K, c.norm_eps, m->a, s);
       A = m->a;
     }
-    launch_gemm_bf16(A, W, M, N, K, ep, s);
+    launch_gemm_f16(A, W, M, N, K, ep, s);
   } else {
     launch_gemv(c.dtype, A, W, norm_w, c.norm_eps, M, N, K, ep, s);
   }
@@ -407,11 +407,22 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   const size_t es = d.es;
   const size_t row = (size_t)d.dim * es;
   hipError_t e = hipSuccess;
-  auto cp = [&](void* dst, const void* src, size_t n) {
-    if (e == hipSuccess) e = hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, s);
+  const bool h = c.dtype == LLM_BF16;
+  // Copy rows [0, rows) of src ([rows][cols]) to dst rows r * mult + off.  The fp32
+  // path copies as is; bf16 weights are stored as fp16 (exact conversion).
+  auto put = [&](void* dst, const void* src, size_t rows, int cols, int mult, int off) {
+    if (e != hipSuccess) return;
+    if (h) {
+      launch_pack_rows(src, dst, rows, cols, mult, off, s);
+    } else if (mult == 1) {
+      e = hipMemcpyAsync((char*)dst + (size_t)off * cols * 4, src, rows * cols * 4, hipMemcpyDeviceToDevice, s);
+    } else {
+      e = hipMemcpy2DAsync((char*)dst + (size_t)off * cols * 4, (size_t)mult * cols * 4, src, (size_t)cols * 4,
+                           (size_t)cols * 4, rows, hipMemcpyDeviceToDevice, s);
+    }
   };
-  cp(m->emb, w->tok_embeddings, (size_t)d.V * row);
-  cp(m->out_w, w->output, (size_t)d.V * row);
+  put(m->emb, w->tok_embeddings, d.V, d.dim, 1, 0);
+  put(m->out_w, w->output, d.V, d.dim, 1, 0);
   launch_to_f32(c.dtype, w->norm, m->final_norm, d.dim, s);
   for (int l = 0; l < d.L; ++l) {
     char* base = m->packed + pl.layer0 + (size_t)l * pl.layer_stride;
@@ -425,16 +436,14 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
     launch_to_f32(c.dtype, w->attention_norm[l], L.attn_norm, d.dim, s);
     launch_to_f32(c.dtype, w->ffn_norm[l], L.ffn_norm, d.dim, s);
     // q|k|v rows concatenated.
-    cp(L.wqkv, w->wq[l], (size_t)d.H * d.hd * row);
-    cp((char*)L.wqkv + (size_t)d.H * d.hd * row, w->wk[l], (size_t)d.G * d.hd * row);
-    cp((char*)L.wqkv + (size_t)(d.H + d.G) * d.hd * row, w->wv[l], (size_t)d.G * d.hd * row);
-    cp(L.wo, w->wo[l], (size_t)d.dim * d.H * d.hd * es);
+    put(L.wqkv, w->wq[l], (size_t)d.H * d.hd, d.dim, 1, 0);
+    put((char*)L.wqkv + (size_t)d.H * d.hd * row, w->wk[l], (size_t)d.G * d.hd, d.dim, 1, 0);
+    put((char*)L.wqkv + (size_t)(d.H + d.G) * d.hd * row, w->wv[l], (size_t)d.G * d.hd, d.dim, 1, 0);
+    put(L.wo, w->wo[l], d.dim, d.H * d.hd, 1, 0);
     // w1 / w3 rows interleaved: packed row 2c = w1 row c, 2c + 1 = w3 row c.
-    if (e == hipSuccess)
-      e = hipMemcpy2DAsync(L.w13, 2 * row, w->w1[l], row, row, d.F, hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess)
-      e = hipMemcpy2DAsync((char*)L.w13 + row, 2 * row, w->w3[l], row, row, d.F, hipMemcpyDeviceToDevice, s);
-    cp(L.w2, w->w2[l], (size_t)d.dim * d.F * es);
+    put(L.w13, w->w1[l], d.F, d.dim, 2, 0);
+    put(L.w13, w->w3[l], d.F, d.dim, 2, 1);
+    put(L.w2, w->w2[l], d.dim, d.F, 1, 0);
   }
   // RoPE tables: angle(pos, j) = pos * theta^(-2j/hd) in fp64, stored as fp32 cos / sin.
   const int half = d.hd / 2;

@@ -66,10 +66,15 @@ class LlamaModel:
             self.handle = None
 
     # ------------------------------------------------------------------ views
+    @property
+    def cache_dtype(self) -> torch.dtype:
+        """Element type of the KV cache: fp16 for bf16-weight models (their compute type), else fp32."""
+        return torch.float16 if self.shape.dtype == "bf16" else torch.float32
+
     def kv_cache_view(self) -> torch.Tensor:
         """[n_layers, 2 (K, V), max_batch, n_kv_heads, max_seq_len, head_dim] view of the cache."""
         s = self.shape
-        return self.kv.view(self.torch_dtype).view(s.n_layers, 2, self.cfg.max_batch, s.n_kv_heads,
+        return self.kv.view(self.cache_dtype).view(s.n_layers, 2, self.cfg.max_batch, s.n_kv_heads,
                                                    s.max_seq_len, s.dim // s.n_heads)
 
     # ------------------------------------------------------------------ calls

@@ -1,0 +1,196 @@
+"""GPU parity at the full Llama-3-8B sizes, in the launch configurations the benchmark uses.
+
+* 32-layer model, prompt of 512 ids: prefill logits and the first decode steps
+  (the GPU fed the oracle's greedy tokens) against the fp32-matmul oracle; the
+  graph-replayed generation loop against direct decode steps.
+* Prefill of 8192 ids: the KV cache the GPU wrote for the first positions against
+  the oracle's prefix run (causality makes those entries independent of later
+  tokens), and the last-position logits against a prefill of 8191 ids plus one
+  decode step (cached decode equals recompute).
+* Batched decode, 64 sequences with cached lengths U{1024..8192} and N(0,1)
+  caches: seeded rows (including the shortest and longest) against the oracle,
+  and every row against a batch-1 decode of the same row.
+
+Tolerance: 2e-2 of max |logit| (bf16 path); greedy tokens equal to the oracle's
+or a certified near-tie.
+"""
+import gc
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+from llama_decoder_transformer_amd import inputs
+from oracle import OracleModel
+
+from helpers import near_tie_ok, oracle_config, rel_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 2e-2
+
+
+def _i32(a):
+    return torch.as_tensor(np.asarray(a, np.int32), device=DEV)
+
+
+def _free():
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def w8b():
+    """bf16 bits of every Llama-3-8B-shaped weight (seed 0) and a lazy fp32 oracle."""
+    shape = inputs.LLAMA3_8B
+    bits = {name: inputs.weight(shape, name) for name in shape.weight_shapes()}
+    cache = {}
+
+    def oracle(max_seq):
+        if "w" not in cache:
+            def cv(item):
+                return item[0], inputs.bf16_bits_to_f32(item[1])
+            with ThreadPoolExecutor(8) as ex:
+                cache["w"] = dict(ex.map(cv, bits.items()))
+        return OracleModel(oracle_config(shape.replace(max_seq_len=max_seq)), cache["w"], dtype=np.float32)
+
+    yield shape, bits, oracle
+    cache.clear()
+
+
+def _gpu_model(shape, bits, max_batch, max_prefill):
+    from llama_decoder_transformer_amd.model import LlamaModel
+    dw = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(DEV) for k, v in bits.items()}
+    m = LlamaModel(shape, dw, max_batch=max_batch, max_prefill_tokens=max_prefill, device=DEV)
+    del dw
+    _free()
+    return m
+
+
+def test_llama3_8b_prefill_512_and_decode_match_oracle(w8b):
+    shape0, bits, oracle = w8b
+    wl = inputs.WORKLOADS["llama3-8b"]
+    shape = wl.shape
+    P = wl.prompt_len
+    prompt = inputs.token_ids(shape.vocab_size, P)
+    n_check = 4
+    om = oracle(shape.max_seq_len)
+    ref_toks, ref_logits = om.generate(prompt, n_check)
+    print(f"[8b prefill 512] oracle tokens {ref_toks.tolist()}", flush=True)
+
+    m = _gpu_model(shape, bits, 1, P)
+    lg = m.prefill(_i32(prompt)).cpu().numpy()
+    errs = [rel_err(lg, ref_logits[0])]
+    ok = [near_tie_ok(int(np.argmax(lg)), ref_logits[0], TOL)]
+    for s in range(n_check):
+        lg = m.decode_step(_i32([0]), _i32([P + s]), _i32([ref_toks[s]])).cpu().numpy()[0]
+        errs.append(rel_err(lg, ref_logits[s + 1]))
+        ok.append(near_tie_ok(int(np.argmax(lg)), ref_logits[s + 1], TOL))
+    print(f"[8b prefill 512] rel errs {np.round(errs, 5).tolist()}, argmax ok {ok}", flush=True)
+    assert max(errs) <= TOL and all(ok)
+
+    # The graph-replayed loop (what the benchmark times) equals direct decode steps, bitwise.
+    logits = m.prefill(_i32(prompt))
+    tok = m.argmax(logits)
+    t0 = int(tok.item())
+    pos = _i32([P])
+    out, last = m.generate(_i32([0]), pos, tok, 8)
+    graph_toks = [t0] + out[:, 0].cpu().tolist()
+    direct = [t0]
+    for s in range(8):
+        lgd = m.decode_step(_i32([0]), _i32([P + s]), _i32([direct[-1]]))
+        direct.append(int(m.argmax(lgd).item()))
+    assert graph_toks == direct
+    assert np.array_equal(last.cpu().numpy(), lgd.cpu().numpy())
+    assert m.read_device_error() == 0
+    del m
+    _free()
+
+
+def test_llama3_8b_prefill_8192(w8b):
+    shape0, bits, oracle = w8b
+    wl = inputs.WORKLOADS["llama3-8b-long-prefill"]
+    shape = wl.shape
+    S = wl.prompt_len
+    prompt = inputs.token_ids(shape.vocab_size, S)
+    m = _gpu_model(shape, bits, 1, S)
+    full = m.prefill(_i32(prompt)).cpu().numpy()
+    assert np.all(np.isfinite(full))
+    kv = m.kv_cache_view()
+    Pfx = 48
+    gpu_k = kv[:, 0, 0, :, :Pfx].float().cpu().numpy()  # [L, G, Pfx, d]
+    gpu_v = kv[:, 1, 0, :, :Pfx].float().cpu().numpy()
+    # cached decode of the last token equals the full prefill's last-position logits
+    m.prefill(_i32(prompt[:-1]))
+    dec = m.decode_step(_i32([0]), _i32([S - 1]), _i32([prompt[-1]])).cpu().numpy()[0]
+    e_dec = rel_err(dec, full)
+    assert int(np.argmax(dec)) == int(np.argmax(full)) or near_tie_ok(int(np.argmax(dec)), full, TOL)
+    del m
+    _free()
+    om = oracle(Pfx)
+    cache = om.new_cache(Pfx)
+    om.prefill(prompt[:Pfx], cache=cache)
+    ek = max(rel_err(gpu_k[l].transpose(1, 0, 2), cache[l][0]) for l in range(shape.n_layers))
+    ev = max(rel_err(gpu_v[l].transpose(1, 0, 2), cache[l][1]) for l in range(shape.n_layers))
+    print(f"[8b prefill 8192] prefix K rel err {ek:.3e}, V rel err {ev:.3e}, decode-vs-prefill {e_dec:.3e}", flush=True)
+    assert ek <= TOL and ev <= TOL and e_dec <= TOL
+
+
+def _fill_cache(kv, shape, lengths, seed):
+    """N(0,1) bf16 cache contents for every (layer, K/V, sequence, kv head), written into kv."""
+    G, hd = shape.n_kv_heads, shape.head_dim
+    B = len(lengths)
+    jobs = [(w, b, g) for w in (0, 1) for b in range(B) for g in range(G)]
+    for l in range(shape.n_layers):
+        def gen(job):
+            w, b, g = job
+            return job, inputs.kv_contents_bf16_bits(l, w, b, g, int(lengths[b]), hd, seed=seed)
+        with ThreadPoolExecutor(16) as ex:
+            for (w, b, g), blk in ex.map(gen, jobs):
+                kv[l, w, b, g, : lengths[b]] = torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16).to(DEV).to(kv.dtype)
+
+
+def test_llama3_8b_batched_decode_64_ragged(w8b):
+    shape0, bits, oracle = w8b
+    wl = inputs.WORKLOADS["llama3-8b-batched-decode"]
+    shape = wl.shape
+    B = wl.batch
+    lo, hi = wl.kv_len_range
+    lengths = inputs.kv_lengths(B, lo, hi)
+    toks = inputs.token_ids(shape.vocab_size, B, sub=4)
+    m = _gpu_model(shape, bits, B, 1)
+    kv = m.kv_cache_view()
+    _fill_cache(kv, shape, lengths, seed=0)
+    slots = _i32(np.arange(B))
+    lg = m.decode_step(slots, _i32(lengths), _i32(toks)).cpu().numpy()
+    assert m.read_device_error() == 0
+    # every row equals a batch-1 decode of the same row (same slot, same cache)
+    worst_bi = 0.0
+    for b in range(B):
+        one = m.decode_step(_i32([b]), _i32([lengths[b]]), _i32([toks[b]])).cpu().numpy()[0]
+        worst_bi = max(worst_bi, rel_err(lg[b], one))
+    # oracle rows: the shortest, the longest and two seeded others
+    rng = np.random.default_rng(11)
+    rows = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), *rng.choice(B, 2, replace=False).tolist()})
+    del m
+    _free()
+    om = oracle(hi + 1)
+    G, hd = shape.n_kv_heads, shape.head_dim
+    errs = []
+    for b in rows:
+        L = int(lengths[b])
+        cache = om.new_cache(L + 1)
+        for l in range(shape.n_layers):
+            for w in (0, 1):
+                blk = np.stack([inputs.kv_contents_bf16_bits(l, w, b, g, L, hd, seed=0) for g in range(G)])
+                cache[l][w][:L] = inputs.bf16_bits_to_f32(blk).transpose(1, 0, 2)
+        ref = om.decode(int(toks[b]), L, cache)
+        errs.append(rel_err(lg[b], ref))
+        assert near_tie_ok(int(np.argmax(lg[b])), ref, TOL)
+    print(f"[8b batched decode] rows {rows} lengths {[int(lengths[r]) for r in rows]} rel errs "
+          f"{np.round(errs, 5).tolist()}, batch-invariance rel err {worst_bi:.3e}", flush=True)
+    assert max(errs) <= TOL and worst_bi <= TOL

@@ -168,7 +168,7 @@ def test_batched_decode_ragged_cache_matches_oracle(batch):
             for which in (0, 1):
                 blk = np.stack([inputs.kv_contents_bf16_bits(l, which, b, g, int(lengths[b]), hd, seed=7)
                                 for g in range(G)])  # [G, L, hd]
-                kv[l, which, b, :, : lengths[b]] = torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16).to(DEV)
+                kv[l, which, b, :, : lengths[b]] = torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16).to(DEV).to(kv.dtype)
                 kvs.append(inputs.bf16_bits_to_f32(blk).transpose(1, 0, 2).astype(np.float64))
             rows.append(kvs)
         host_cache.append(rows)
