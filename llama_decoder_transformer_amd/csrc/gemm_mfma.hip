@@ -5,66 +5,108 @@
 // are rounded to fp16 rather than bf16: same bytes and MFMA rate, 8x finer
 // rounding, which keeps 32 layers within the bf16 parity bar.
 //
-// Tiling: BM x BN output tile per 256-thread workgroup (4 waves as 2 x 2), BK =
-// 64 per stage, v_mfma_f32_16x16x32_f16 on 16x16 blocks.  A lane feeds row
-// (lane % 16) and the 8 k-values starting at 8 * (lane / 16) of a 16x32 block;
-// it receives rows 4 * (lane / 16) + r, r = 0..3, of column lane % 16 of the
-// 16x16 result.  The epilogue therefore sees RoPE partners (columns 2j, 2j+1)
-// and SwiGLU gate/up pairs (packed columns 2c, 2c+1) in lanes l and l ^ 1.
-// LDS rows are padded by 16 bytes so the fragment reads of 16 consecutive rows
-// spread over the banks.
+// Tiling: BM x BN output tile per 256-thread workgroup (4 waves as 2 x 2, each
+// owning a BM/2 x BN/2 sub-tile), BK = 64 per stage, v_mfma_f32_16x16x32_f16 on
+// 16x16 blocks.  A lane feeds row (lane % 16) and the 8 k-values starting at
+// 8 * (lane / 16) of a 16x32 block; it receives rows 4 * (lane / 16) + r,
+// r = 0..3, of column lane % 16 of the 16x16 result.  The epilogue therefore
+// sees RoPE partners (columns 2j, 2j+1) and SwiGLU gate/up pairs (packed columns
+// 2c, 2c+1) in lanes l and l ^ 1.
+//
+// Pipeline: two LDS stages; while the waves run the MFMAs of stage k, the global
+// loads of stage k+1 are in flight in registers and are written to the other
+// stage afterwards, so each K step needs one barrier.  LDS tiles use an XOR
+// swizzle of the 16-byte chunks (lds_off) instead of padding.
+//
+// Tile order: workgroups are dealt to the 8 XCDs round-robin, so the 1-D grid
+// index is remapped so that each XCD receives a contiguous run of tiles, ordered
+// N-tile-major: the M tiles that share a weight tile run on the same XCD (one L2)
+// at about the same time and the weights are fetched from HBM once.
 #include "common.h"
 #include "epilogue.h"
 #include "launch.h"
 
 namespace llm {
 
-template <int BM, int BN, int EPI>
-__global__ void __launch_bounds__(256) gemm_f16_kernel(const f16_t* __restrict__ A, const f16_t* __restrict__ W,
-                                                        int M, int N, int K, EpiParams ep) {
-  constexpr int BK = 64;
-  constexpr int LDK = BK + 8;  // padded LDS row (144 bytes)
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int A_LD = BM * BK / 8 / 256;  // 16-byte loads per thread per stage
-  constexpr int B_LD = BN * BK / 8 / 256;
-  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads");
+constexpr int GEMM_BK = 64;
+constexpr int GEMM_LDK = GEMM_BK;  // LDS row = 128 bytes = 8 chunks of 16 bytes
 
-  __shared__ __attribute__((aligned(16))) f16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) f16_t Bs[BN * LDK];
+// LDS position of 16-byte chunk c (0..7) of tile row r: rows are not padded;
+// the chunk index is XORed with (r / 2) % 8 so that the 16 lanes of a fragment
+// read (16 consecutive rows, one chunk) and of a tile store (2 rows, 8 chunks
+// each) hit distinct banks.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * GEMM_LDK + ((c ^ ((r >> 1) & 7)) << 3); }
+
+template <int BM, int BN, int WGM, int WGN, int EPI, int NPART = 1, bool SB = false>
+__global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* __restrict__ A,
+                                                                  const f16_t* __restrict__ W, int M, int N, int K,
+                                                                  int tiles_m, int tiles_n, EpiParams ep) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int BK = GEMM_BK, LDK = GEMM_LDK;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int A_LD = BM * BK / 8 / NT;  // 16-byte loads per thread per stage
+  constexpr int B_LD = BN * BK / 8 / NT;
+  static_assert(A_LD >= 1 && B_LD >= 1 && A_LD * NT * 8 == BM * BK && B_LD * NT * 8 == BN * BK,
+                "tile does not split evenly over the threads");
+  constexpr int STAGE = (BM + BN) * LDK;  // f16 elements per LDS stage
+
+  extern __shared__ __attribute__((aligned(16))) f16_t smem[];
+
+  // XCD-aware tile order (see the file header).
+  const int T = tiles_m * tiles_n;
+  const int id = blockIdx.x;
+  const int per = T / 8, rem = T % 8;
+  const int xcd = id % 8, j = id / 8;
+  const int t = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + j;
+  const int tn_idx = t / tiles_m, tm_idx = t % tiles_m;
+  const int tm = tm_idx * BM, tn = tn_idx * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  const int tm = blockIdx.y * BM, tn = blockIdx.x * BN;
+  const int wm = wid / WGN, wn = wid % WGN;
   const int l16 = lane & 15, lg = lane >> 4;
 
-  u32x4_t ra[A_LD], rb[B_LD];
+  // The next stage's global loads are split into NPART parts, one per k-step of
+  // 32, so only 1/NPART of a stage sits in registers at a time.
+  static_assert((BK / 32) % NPART == 0 && A_LD % NPART == 0 && B_LD % NPART == 0, "bad NPART");
+  constexpr int PA = A_LD / NPART, PB = B_LD / NPART;
+  u32x4_t ra[PA], rb[PB];
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
-  auto gload = [&](int k0) {
+  // Out-of-range rows / columns load from a clamped in-range address and are then
+  // replaced by zero with a select, so the loads stay branch-free.
+  auto gload = [&](int k0, int part) {
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int idx = tid + i * 256, r = idx >> 3, c = (idx & 7) * 8;
+    for (int i = 0; i < PA; ++i) {
+      const int idx = tid + (part * PA + i) * NT, r = idx >> 3, c = (idx & 7) * 8;
       const int gm = tm + r, gk = k0 + c;
-      ra[i] = (gm < M && gk < K) ? *reinterpret_cast<const u32x4_t*>(A + (size_t)gm * K + gk) : zero;
+      const bool ok = gm < M && gk < K;
+      const u32x4_t v =
+          *reinterpret_cast<const u32x4_t*>(A + (size_t)min(gm, M - 1) * K + min(gk, K - 8));
+      ra[i] = ok ? v : zero;
     }
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int idx = tid + i * 256, r = idx >> 3, c = (idx & 7) * 8;
+    for (int i = 0; i < PB; ++i) {
+      const int idx = tid + (part * PB + i) * NT, r = idx >> 3, c = (idx & 7) * 8;
       const int gn = tn + r, gk = k0 + c;
-      rb[i] = (gn < N && gk < K) ? *reinterpret_cast<const u32x4_t*>(W + (size_t)gn * K + gk) : zero;
+      const bool ok = gn < N && gk < K;
+      const u32x4_t v =
+          *reinterpret_cast<const u32x4_t*>(W + (size_t)min(gn, N - 1) * K + min(gk, K - 8));
+      rb[i] = ok ? v : zero;
     }
   };
-  auto sstore = [&]() {
+  auto sstore = [&](int stage, int part) {
+    f16_t* As = smem + stage * STAGE;
+    f16_t* Bs = As + BM * LDK;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int idx = tid + i * 256, r = idx >> 3, c = (idx & 7) * 8;
-      *reinterpret_cast<u32x4_t*>(&As[r * LDK + c]) = ra[i];
+    for (int i = 0; i < PA; ++i) {
+      const int idx = tid + (part * PA + i) * NT, r = idx >> 3, c = (idx & 7) * 8;
+      *reinterpret_cast<u32x4_t*>(&As[lds_off(r, c >> 3)]) = ra[i];
     }
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int idx = tid + i * 256, r = idx >> 3, c = (idx & 7) * 8;
-      *reinterpret_cast<u32x4_t*>(&Bs[r * LDK + c]) = rb[i];
+    for (int i = 0; i < PB; ++i) {
+      const int idx = tid + (part * PB + i) * NT, r = idx >> 3, c = (idx & 7) * 8;
+      *reinterpret_cast<u32x4_t*>(&Bs[lds_off(r, c >> 3)]) = rb[i];
     }
   };
 
@@ -72,42 +114,54 @@ __global__ void __launch_bounds__(256) gemm_f16_kernel(const f16_t* __restrict__
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = (K + BK - 1) / BK;
-  gload(0);
+#pragma unroll
+  for (int part = 0; part < NPART; ++part) {
+    gload(0, part);
+    sstore(0, part);
+  }
+  __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    sstore();
-    __syncthreads();
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    const f16_t* As = smem + cur * STAGE;
+    const f16_t* Bs = As + BM * LDK;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
+      constexpr int KS_PER_PART = (BK / 32) / NPART;
+      if (more && ks % KS_PER_PART == 0) gload((kt + 1) * BK, ks / KS_PER_PART);
       f16x8_t af[FM], bw[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const f16x8_t*>(&As[(wm * WM + i * 16 + l16) * LDK + ks * 32 + lg * 8]);
+        af[i] = *reinterpret_cast<const f16x8_t*>(&As[lds_off(wm * WM + i * 16 + l16, ks * 4 + lg)]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bw[j] = *reinterpret_cast<const f16x8_t*>(&Bs[(wn * WN + j * 16 + l16) * LDK + ks * 32 + lg * 8]);
+      for (int jn = 0; jn < FN; ++jn)
+        bw[jn] = *reinterpret_cast<const f16x8_t*>(&Bs[lds_off(wn * WN + jn * 16 + l16, ks * 4 + lg)]);
+      // Keep every fragment read of this k-step ahead of its MFMAs (the scheduler
+      // otherwise reuses one register set and waits on each read in turn).
+      if (SB) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bw[j], acc[i][j], 0, 0, 0);
+        for (int jn = 0; jn < FN; ++jn)
+          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bw[jn], acc[i][jn], 0, 0, 0);
+      if (more && ks % KS_PER_PART == KS_PER_PART - 1) sstore(cur ^ 1, ks / KS_PER_PART);
     }
+    __syncthreads();
   }
 
   // Epilogue.
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+    for (int jn = 0; jn < FN; ++jn) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = tm + wm * WM + i * 16 + lg * 4 + r;
-        const int n = tn + wn * WN + j * 16 + l16;
-        const float v = acc[i][j][r];
+        const int n = tn + wn * WN + jn * 16 + l16;
+        const float v = acc[i][jn][r];
         if (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
           const float vp = __shfl_xor(v, 1);
           if (m < M && n < N) {
@@ -124,23 +178,69 @@ __global__ void __launch_bounds__(256) gemm_f16_kernel(const f16_t* __restrict__
 }
 
 template <int BM, int BN>
+static size_t gemm_lds_bytes() {
+  return (size_t)2 * (BM + BN) * GEMM_LDK * sizeof(f16_t);
+}
+
+template <int BM, int BN, int WGM, int WGN, int NPART = 1, bool SB = false>
 static void gemm_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep, hipStream_t s) {
-  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const dim3 grid(tm * tn);
+  const int nt = 64 * WGM * WGN;
+  const size_t lds = gemm_lds_bytes<BM, BN>();
   switch (ep.kind) {
-    case EPI_STORE_F32: gemm_f16_kernel<BM, BN, EPI_STORE_F32><<<grid, 256, 0, s>>>(A, W, M, N, K, ep); break;
-    case EPI_RESID: gemm_f16_kernel<BM, BN, EPI_RESID><<<grid, 256, 0, s>>>(A, W, M, N, K, ep); break;
-    case EPI_QKV: gemm_f16_kernel<BM, BN, EPI_QKV><<<grid, 256, 0, s>>>(A, W, M, N, K, ep); break;
-    case EPI_SWIGLU: gemm_f16_kernel<BM, BN, EPI_SWIGLU><<<grid, 256, 0, s>>>(A, W, M, N, K, ep); break;
+    case EPI_STORE_F32:
+      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_STORE_F32, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep);
+      break;
+    case EPI_RESID:
+      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_RESID, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep);
+      break;
+    case EPI_QKV:
+      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_QKV, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep);
+      break;
+    case EPI_SWIGLU:
+      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_SWIGLU, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep);
+      break;
   }
 }
 
+template <int BM, int BN, int WGM, int WGN, int NPART = 1, bool SB = false>
+static void gemm_set_lds_limit() {
+  const int bytes = (int)gemm_lds_bytes<BM, BN>();
+  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_STORE_F32, NPART, SB>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_RESID, NPART, SB>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_QKV, NPART, SB>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_SWIGLU, NPART, SB>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+// Tiles above 64 KiB of LDS need the per-kernel dynamic limit raised once.
+static void gemm_init_attributes() {
+  static bool done = false;
+  if (done) return;
+  done = true;
+  gemm_set_lds_limit<256, 256, 2, 4, 1, true>();
+  gemm_set_lds_limit<128, 128, 2, 2>();
+}
+
+// Tile choice from a sweep of the Llama-3-8B projection shapes at M = 512, 2048
+// and 8192 on MI355X: the 8-wave 256 x 256 tile when it still yields at least 192
+// tiles, then 128 x 128 with at least 256 tiles (one per CU), else 64 x 64.
 void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
-  const long tiles128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (M > 64 && tiles128 >= 512)
-    gemm_dispatch<128, 128>((const f16_t*)A, (const f16_t*)W, M, N, K, ep, s);
+  gemm_init_attributes();
+  const f16_t* a = (const f16_t*)A;
+  const f16_t* w = (const f16_t*)W;
+  auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (M > 128 && tiles(256, 256) >= 192)
+    gemm_dispatch<256, 256, 2, 4, 1, true>(a, w, M, N, K, ep, s);
+  else if (M > 64 && tiles(128, 128) >= 256)
+    gemm_dispatch<128, 128, 2, 2>(a, w, M, N, K, ep, s);
   else
-    gemm_dispatch<64, 64>((const f16_t*)A, (const f16_t*)W, M, N, K, ep, s);
+    gemm_dispatch<64, 64, 2, 2>(a, w, M, N, K, ep, s);
 }
 
 }  // namespace llm
