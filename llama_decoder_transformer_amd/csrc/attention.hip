@@ -27,9 +27,9 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 //
 // Grid (chunk, kv-head x head-block, row).  A workgroup handles one row (decode
 // sequence or prefill token), one KV head, up to 4 of its query heads, and the
-// CH keys of one chunk.  16 groups of 16 lanes each take 4 keys per round of 64
-// (all 8 K/V loads of a round are issued before any arithmetic), a lane holding
-// d/16 elements (16 bytes for fp16 d = 128).  Each group keeps its own running
+// CH keys of one chunk.  Groups of 16 lanes each take 4 keys per round
+// (the loads of the next round are issued before the current one is consumed),
+// a lane holding d/16 elements (16 bytes for fp16 d = 128).  Each group keeps its own running
 // max / sum / accumulator; the groups are merged through LDS.  A row whose keys
 // fit one chunk is written out directly; otherwise each chunk writes a partial
 // (max, sum, acc[d]) that attn_combine_kernel merges.  (Merging in the last
@@ -49,6 +49,30 @@ __device__ __forceinline__ void load_epl(const T* p, float* out) {
   }
 }
 
+// One key row slice of a lane: d/16 elements, kept raw (one 16-byte word for
+// fp16 d = 128) from the load until the math so that a round's loads can be in
+// flight while the previous round is consumed.
+template <typename T, int EPL>
+struct KeySlice {
+  float v[EPL];
+  __device__ __forceinline__ void load(const T* p) { load_epl<T, EPL>(p, v); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] = 0.f;
+  }
+  __device__ __forceinline__ void get(float* o) const {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = v[e];
+  }
+};
+template <>
+struct KeySlice<f16_t, 8> {
+  u32x4_t raw;
+  __device__ __forceinline__ void load(const f16_t* p) { raw = *reinterpret_cast<const u32x4_t*>(p); }
+  __device__ __forceinline__ void zero() { raw = u32x4_t{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void get(float* o) const { f16x8_to_f32(raw, o); }
+};
+
 template <typename T, int D, int NT, int MAXH>
 __global__ void __launch_bounds__(NT) attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc,
                                                          const T* __restrict__ vc, const int* __restrict__ row_pos,
@@ -56,10 +80,15 @@ __global__ void __launch_bounds__(NT) attn_decode_kernel(const T* __restrict__ q
                                                          int H, int G, int max_seq, int n_slots, int CH, int nchunks,
                                                          int hpb, float* partial, T* __restrict__ out, int* err) {
   constexpr int EPL = D / 16;
-  constexpr int NG = NT / 16;  // groups of 16 lanes
+  constexpr int NG = NT / 16;                 // groups of 16 lanes
+  constexpr int GPP = NG >= 64 ? 8 : NG;      // groups merged per part in the first merge level
+  constexpr int PARTS = NG / GPP;
   __shared__ float s_m[NG][MAXH];
   __shared__ float s_l[NG][MAXH];
   __shared__ float s_acc[NG][MAXH][D];
+  __shared__ float s_M[MAXH];
+  __shared__ float s_pa[PARTS][MAXH][D];
+  __shared__ float s_pl[PARTS][MAXH];
 
   const int chunk = blockIdx.x, gy = blockIdx.y, row = blockIdx.z;
   const int hpg = H / G;
@@ -87,6 +116,24 @@ __global__ void __launch_bounds__(NT) attn_decode_kernel(const T* __restrict__ q
   const T* kb = kc + base;
   const T* vb = vc + base;
 
+  KeySlice<T, EPL> kf[2][4], vf[2][4];
+  bool ok[2][4];
+  auto fetch = [&](int buf, int r0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j = r0 + grp + NG * t;
+      ok[buf][t] = j < end;
+      if (ok[buf][t]) {
+        kf[buf][t].load(kb + (size_t)j * D + gl * EPL);
+        vf[buf][t].load(vb + (size_t)j * D + gl * EPL);
+      } else {
+        kf[buf][t].zero();
+        vf[buf][t].zero();
+      }
+    }
+  };
+  fetch(0, start);
+
   float qv[MAXH][EPL];
 #pragma unroll
   for (int hh = 0; hh < MAXH; ++hh) {
@@ -105,20 +152,12 @@ __global__ void __launch_bounds__(NT) attn_decode_kernel(const T* __restrict__ q
     for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
   }
 
-  for (int r0 = start; r0 < end; r0 += 4 * NG) {
+  auto consume = [&](int buf) {
     float kv[4][EPL], vv[4][EPL];
-    bool ok[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int j = r0 + grp + NG * t;
-      ok[t] = j < end;
-      if (ok[t]) {
-        load_epl<T, EPL>(kb + (size_t)j * D + gl * EPL, kv[t]);
-        load_epl<T, EPL>(vb + (size_t)j * D + gl * EPL, vv[t]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) { kv[t][e] = 0.f; vv[t][e] = 0.f; }
-      }
+      kf[buf][t].get(kv[t]);
+      vf[buf][t].get(vv[t]);
     }
 #pragma unroll
     for (int hh = 0; hh < MAXH; ++hh) {
@@ -133,7 +172,7 @@ __global__ void __launch_bounds__(NT) attn_decode_kernel(const T* __restrict__ q
           d += __shfl_xor(d, 4);
           d += __shfl_xor(d, 2);
           d += __shfl_xor(d, 1);
-          sc[t] = ok[t] ? d : -INFINITY;
+          sc[t] = ok[buf][t] ? d : -INFINITY;
         }
         const float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         const float mn = fmaxf(mx[hh], mloc);
@@ -152,8 +191,23 @@ __global__ void __launch_bounds__(NT) attn_decode_kernel(const T* __restrict__ q
         mx[hh] = mn;
       }
     }
+  };
+
+  // Rounds of 4 * NG keys, two register sets: the next round's loads are issued
+  // before the current round is consumed.
+  for (int r0 = start; r0 < end; r0 += 8 * NG) {
+    const bool more1 = r0 + 4 * NG < end;
+    if (more1) fetch(1, r0 + 4 * NG);
+    consume(0);
+    if (!more1) break;
+    const bool more2 = r0 + 8 * NG < end;
+    if (more2) fetch(0, r0 + 8 * NG);
+    consume(1);
+    if (!more2) break;
   }
 
+  // Merge the groups: per-head maximum, then PARTS partial sums of GPP groups each,
+  // then the parts.
 #pragma unroll
   for (int hh = 0; hh < MAXH; ++hh) {
     if (hh < hpb) {
@@ -163,22 +217,46 @@ __global__ void __launch_bounds__(NT) attn_decode_kernel(const T* __restrict__ q
     }
   }
   __syncthreads();
-  for (int t = tid; t < hpb * D; t += NT) {
-    const int hh = t / D, e = t % D;
-    float M = -1e30f;
-    for (int i = 0; i < NG; ++i) M = fmaxf(M, s_m[i][hh]);
+  if (tid < 64) {
+#pragma unroll
+    for (int hh = 0; hh < MAXH; ++hh) {
+      if (hh < hpb) {
+        const float v = tid < NG ? s_m[tid][hh] : -1e30f;
+        const float M = wave_max(v);
+        if (tid == 0) s_M[hh] = M;
+      }
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < PARTS * hpb * D; t += NT) {
+    const int part = t / (hpb * D), rem = t % (hpb * D);
+    const int hh = rem / D, e = rem % D;
+    const float M = s_M[hh];
     float L = 0.f, a = 0.f;
-    for (int i = 0; i < NG; ++i) {
+#pragma unroll 8
+    for (int i = part * GPP; i < part * GPP + GPP; ++i) {
       const float w = exp2f(s_m[i][hh] - M);
       L += s_l[i][hh] * w;
       a += s_acc[i][hh][e] * w;
+    }
+    s_pa[part][hh][e] = a;
+    if (e == 0) s_pl[part][hh] = L;
+  }
+  __syncthreads();
+  for (int t = tid; t < hpb * D; t += NT) {
+    const int hh = t / D, e = t % D;
+    float L = 0.f, a = 0.f;
+#pragma unroll
+    for (int part = 0; part < PARTS; ++part) {
+      L += s_pl[part][hh];
+      a += s_pa[part][hh][e];
     }
     if (nvalid == 1) {
       orow[(size_t)(h0 + hh) * D + e] = from_f32<T>(a / L);
     } else {
       float* pr = partial + (((size_t)row * H + h0 + hh) * nchunks + chunk) * (D + 2);
       pr[e] = a;
-      if (e == 0) { pr[D] = M; pr[D + 1] = L; }
+      if (e == 0) { pr[D] = s_M[hh]; pr[D + 1] = L; }
     }
   }
 }
