@@ -1,19 +1,25 @@
 #!/usr/bin/env python3
 """Throughput of the Llama decoder pass on one MI355X.
 
-Default workload: the Llama-3-8B shape (32 layers, dim 4096, 32 query / 8 KV
-heads, FFN 14336, vocab 128256, bf16 random-init weights ~ N(0, 0.02)), batch 1,
-a prompt of 512 token ids uniform in [0, 128256), prefill, then 256 greedy
-KV-cached decode steps.  One step = that whole job; the JSON line reports
-tokens/s over it plus prefill tok/s and decode tok/s separately.
+Default workload (``--workload llama3-8b``): the Llama-3-8B shape (32 layers,
+dim 4096, 32 query / 8 KV heads, FFN 14336, vocab 128256, bf16 random-init
+weights ~ N(0, 0.02)), batch 1, a prompt of 512 token ids uniform in
+[0, 128256), prefill, then 256 greedy KV-cached decode steps replayed from the
+library's HIP graph.  One step = that whole job; the JSON line reports tokens/s
+over it plus prefill tok/s and decode tok/s separately.
 
-Per-kernel durations come from the library's own hipEvent brackets (one
-extra, untimed step run with kernel timing on); the roofline object is for the
-dominant kernel (the decode gate-up projection, HBM-bound), with the prefill
-gate-up GEMM (MFMA-bound) reported next to it.  ``cpu_baseline`` times the CPU
-oracle on a bounded sample of the same workload and scales it to the full job.
+Other workloads (opt-in, same JSON contract):
+  llama3-8b-layer           one 8B-shaped layer on x ~ N(0,1) [2048, 4096] (prefill tok/s)
+  llama3-8b-long-prefill    prefill of 8192 ids, last-position logits (prefill tok/s)
+  llama3-8b-batched-decode  one decode step of 64 sequences, cached lengths U{1024..8192},
+                            N(0,1) caches (decode tok/s)
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Per-kernel durations come from the library's own hipEvent brackets (one extra,
+untimed pass with kernel timing on); ``roofline`` is for the workload's dominant
+kernel.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload and scales it to the full job.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -29,15 +35,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
+METRIC = "prefill tok/s + decode tok/s at Llama-3-8B shape, % of MFMA/HBM roofline"
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def make_weights(shape, keep_layers: int):
-    """Device bf16 weights for every tensor; host float32 copies of a few layers for the CPU sample."""
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
+def make_weights(shape, keep_layers: int, keep_head: bool = True):
+    """Device bf16 weights for every tensor; host float32 copies of the first layers for the CPU sample."""
     import torch
 
     from llama_decoder_transformer_amd import inputs
@@ -47,24 +62,156 @@ def make_weights(shape, keep_layers: int):
         bits = inputs.weight(shape, name)
         dev[name] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
         layer = int(name.split(".")[1]) if name.startswith("layers.") else -1
-        if layer < keep_layers:
+        if (layer >= 0 and layer < keep_layers) or (layer < 0 and keep_head):
             host[name] = inputs.bf16_bits_to_f32(bits)
     return dev, host
 
 
-def cpu_baseline(shape, host_w, prompt, n_layers_sample: int, decode_sample: int, decode_steps: int):
-    """The oracle (fp32 matmuls) on n_layers_sample of the layers, scaled to the whole model."""
-    from oracle import OracleConfig, OracleModel
+def oracle_cfg(shape, n_layers: int):
+    from oracle import OracleConfig
+    return OracleConfig(dim=shape.dim, n_layers=n_layers, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
+                        vocab_size=shape.vocab_size, ffn_hidden_dim=shape.ffn_hidden_dim,
+                        max_seq_len=shape.max_seq_len, rope_theta=shape.rope_theta, norm_eps=shape.norm_eps)
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    cfg = OracleConfig(dim=shape.dim, n_layers=n_layers_sample, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
-                       vocab_size=shape.vocab_size, ffn_hidden_dim=shape.ffn_hidden_dim,
-                       max_seq_len=shape.max_seq_len, rope_theta=shape.rope_theta, norm_eps=shape.norm_eps)
-    om = OracleModel(cfg, host_w, dtype=np.float32)
+
+def timed_groups(B, h, fn):
+    """Run fn with the library's kernel brackets on; return {group: (launches, total_ms)}."""
+    B.llm_set_kernel_timing(h, True)
+    fn()
+    res = {name: B.llm_kernel_timing(h, k) for k, name in enumerate(B.KERNEL_GROUPS)}
+    B.llm_set_kernel_timing(h, False)
+    return res
+
+
+def per_kernel_table(groups: dict, label: str) -> dict:
+    return {name: {f"{label}_launches": n, f"{label}_avg_us": round(ms / n * 1e3, 2) if n else None}
+            for name, (n, ms) in groups.items() if n}
+
+
+def avg_ms(groups: dict, name: str) -> float:
+    n, ms = groups[name]
+    return ms / n
+
+
+def mfma_roofline(kernel: str, flops: float, ms: float) -> dict:
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "traffic": None, "flops_per_launch": flops,
+            "avg_launch_us": round(ms * 1e3, 2)}
+
+
+def hbm_roofline(kernel: str, nbytes: float, ms: float, traffic=None) -> dict:
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "bytes_per_launch": int(nbytes),
+            "avg_launch_us": round(ms * 1e3, 2)}
+
+
+def layer_flops(shape, S: int) -> tuple[float, float]:
+    """(linear, causal attention) flops of one layer over S positions starting at 0."""
+    d, H, G, F, hd = shape.dim, shape.n_heads, shape.n_kv_heads, shape.ffn_hidden_dim, shape.head_dim
+    lin = 2.0 * S * (d * (H + 2 * G) * hd + H * hd * d + 3 * F * d)
+    att = 4.0 * H * hd * S * (S + 1) / 2
+    return lin, att
+
+
+def time_steps(torch, step, steps: int, warmup: int):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def bench_generate(args, torch, B, inputs, LlamaModel) -> dict:
+    wl = inputs.WORKLOADS["llama3-8b"]
+    shape = wl.shape
+    P, T = wl.prompt_len, wl.decode_steps
+    dev = "cuda:0"
+    t0 = time.perf_counter()
+    dw, host_w = make_weights(shape, 0 if args.no_cpu_baseline else args.cpu_layers)
+    log(f"weights generated and uploaded in {time.perf_counter() - t0:.1f}s")
+    model = LlamaModel(shape, dw, max_batch=1, max_prefill_tokens=P, device=dev)
+    del dw
+    torch.cuda.empty_cache()
+
+    prompt_np = inputs.token_ids(shape.vocab_size, P)
+    prompt = torch.as_tensor(prompt_np, device=dev)
+    slots = torch.zeros(1, dtype=torch.int32, device=dev)
+    pos = torch.zeros(1, dtype=torch.int32, device=dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    logits1 = torch.empty(shape.vocab_size, dtype=torch.float32, device=dev)
+    logitsB = torch.empty(1, shape.vocab_size, dtype=torch.float32, device=dev)
+    out = torch.empty(T, 1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    h = model.handle
+    evs = []
+
+    def step():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        B.llm_prefill(h, 0, prompt, P, 0, logits1, stream)
+        B.llm_argmax(logits1, 1, shape.vocab_size, tok, stream)
+        ev[1].record(stream)
+        pos.fill_(P)
+        B.llm_generate(h, 1, slots, pos, tok, T, out, logitsB, stream)
+        ev[2].record(stream)
+        evs.append(ev)
+
+    wall = time_steps(torch, step, args.steps, args.warmup)
+    evs = evs[args.warmup:]
+    prefill_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    assert model.read_device_error() == 0
+    log(f"timed {args.steps} steps in {wall:.3f}s: prefill {prefill_ms:.3f} ms, decode {decode_ms / T:.3f} ms/token")
+
+    kt_prefill = timed_groups(B, h, lambda: B.llm_prefill(h, 0, prompt, P, 0, logits1, stream))
+    torch.cuda.synchronize()
+    pos.fill_(P)
+    kt_decode = timed_groups(B, h, lambda: B.llm_generate(h, 1, slots, pos, tok, T, out, logitsB, stream))
+    torch.cuda.synchronize()
+
+    L, dim, F, V = shape.n_layers, shape.dim, shape.ffn_hidden_dim, shape.vocab_size
+    up_bytes = 2 * F * dim * 2 + 2 * dim * 4 + F * 2  # w1|w3 weights + fp32 x and norm weight in + SwiGLU row out
+    per_kernel = per_kernel_table(kt_prefill, "prefill")
+    for k, v in per_kernel_table(kt_decode, "decode").items():
+        per_kernel.setdefault(k, {}).update(v)
+    hd = shape.head_dim
+    kv_pos_bytes = L * shape.n_kv_heads * hd * 2 * 2
+    w_bytes = 2 * (L * (dim * (shape.n_heads + 2 * shape.n_kv_heads) * hd + dim * shape.n_heads * hd + 3 * F * dim)
+                   + V * dim)
+    mean_ctx = P + (T - 1) / 2.0 + 1
+    dec_bytes = w_bytes + kv_pos_bytes * mean_ctx
+    res = {
+        "value": round((P + T) * args.steps / wall, 3), "unit": "tok/s", "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "config": {"workload": "llama3-8b: 32-layer Llama-3-8B-shaped bf16 model, batch 1, prefill of 512 ids "
+                               "then 256 greedy KV-cached decode steps",
+                   "prompt_len": P, "decode_steps": T, "batch": 1, "parallelism": "none (1 GPU)"},
+        "prefill_tok_s": round(P / (prefill_ms * 1e-3), 1),
+        "decode_tok_s": round(T / (decode_ms * 1e-3), 2),
+        "prefill_ms": round(prefill_ms, 3),
+        "decode_ms_per_token": round(decode_ms / T, 4),
+        "decode_step_hbm_frac": round(dec_bytes / (decode_ms / T * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": hbm_roofline("decode gate-up projection (w1|w3 GEMV + fused RMSNorm + SwiGLU), M=1", up_bytes,
+                                 avg_ms(kt_decode, "gate_up")),
+        "roofline_prefill": mfma_roofline("prefill gate-up GEMM (M=512, N=28672, K=4096) + SwiGLU",
+                                          2.0 * P * (2 * F) * dim, avg_ms(kt_prefill, "gate_up")),
+        "per_kernel": per_kernel,
+        "generated_first_tokens": out[:8, 0].cpu().tolist(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_generate(shape, host_w, prompt_np, args.cpu_layers, 4, T)
+    return res
+
+
+def cpu_generate(shape, host_w, prompt, n_layers_sample: int, decode_sample: int, decode_steps: int) -> dict:
+    from oracle import OracleModel
+    om = OracleModel(oracle_cfg(shape, n_layers_sample), host_w, dtype=np.float32)
     cache = om.new_cache()
     n = len(prompt)
     t0 = time.perf_counter()
@@ -73,8 +220,7 @@ def cpu_baseline(shape, host_w, prompt, n_layers_sample: int, decode_sample: int
     logits = om.logits_of(h[-1:])[0]
     t2 = time.perf_counter()
     tok = int(np.argmax(logits))
-    t_dec_layers = 0.0
-    t_dec_head = 0.0
+    t_layers = t_head = 0.0
     for s in range(decode_sample):
         a = time.perf_counter()
         hd = om.hidden(om.embed([tok]), cache, np.array([n + s]))
@@ -82,24 +228,206 @@ def cpu_baseline(shape, host_w, prompt, n_layers_sample: int, decode_sample: int
         lg = om.logits_of(hd)[0]
         c = time.perf_counter()
         tok = int(np.argmax(lg))
-        t_dec_layers += b - a
-        t_dec_head += c - b
+        t_layers += b - a
+        t_head += c - b
     scale = shape.n_layers / n_layers_sample
     t_prefill = (t1 - t0) * scale + (t2 - t1)
-    t_decode_step = (t_dec_layers * scale + t_dec_head) / decode_sample
-    total = t_prefill + decode_steps * t_decode_step
-    return {
-        "value": round((n + decode_steps) / total, 3),
-        "unit": "tok/s",
-        "cores": int(cores),
-        "kind": "oracle",
-        "sample": (f"oracle (numpy fp32 matmuls, fp64 norms/softmax) on {n_layers_sample} of {shape.n_layers} layers: "
-                   f"prefill of the {n}-token prompt + {decode_sample} decode steps, plus the LM head; layer time "
-                   f"scaled by {scale:g} to the full model and decode time by {decode_steps}/{decode_sample}"),
-        "prefill_tok_s": round(n / t_prefill, 3),
-        "decode_tok_s": round(1.0 / t_decode_step, 4),
-        "sample_seconds": round(t2 - t0 + t_dec_layers + t_dec_head, 2),
-    }
+    t_step = (t_layers * scale + t_head) / decode_sample
+    total = t_prefill + decode_steps * t_step
+    return {"value": round((n + decode_steps) / total, 3), "unit": "tok/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": (f"oracle (numpy fp32 matmuls, fp64 norms/softmax) on {n_layers_sample} of {shape.n_layers} "
+                       f"layers: prefill of the {n}-token prompt + {decode_sample} decode steps, plus the LM head; "
+                       f"layer time scaled by {scale:g} and decode time by {decode_steps}/{decode_sample}"),
+            "prefill_tok_s": round(n / t_prefill, 3), "decode_tok_s": round(1.0 / t_step, 4),
+            "sample_seconds": round(t2 - t0 + t_layers + t_head, 2)}
+
+
+def bench_layer(args, torch, B, inputs, LlamaModel) -> dict:
+    wl = inputs.WORKLOADS["llama3-8b-layer"]
+    shape = wl.shape.replace(vocab_size=256)  # embedding / LM head unused by the layer
+    S = wl.prompt_len
+    dw, host_w = make_weights(shape, 1 if not args.no_cpu_baseline else 0, keep_head=False)
+    model = LlamaModel(shape, dw, max_batch=1, max_prefill_tokens=S)
+    del dw
+    torch.cuda.empty_cache()
+    x0 = torch.from_numpy(inputs.bf16_bits_to_f32(inputs.activations_bf16_bits(S, shape.dim))).to("cuda:0")
+    x = torch.empty_like(x0)
+    stream = torch.cuda.current_stream()
+    h = model.handle
+    evs = []
+
+    def step():
+        x.copy_(x0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        B.llm_layer_forward(h, 0, 0, x, S, 0, stream)
+        ev[1].record(stream)
+        evs.append(ev)
+
+    wall = time_steps(torch, step, args.steps, args.warmup)
+    layer_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs[args.warmup:]]))
+    x.copy_(x0)
+    kt = timed_groups(B, h, lambda: B.llm_layer_forward(h, 0, 0, x, S, 0, stream))
+    lin, att = layer_flops(shape, S)
+    F, dim = shape.ffn_hidden_dim, shape.dim
+    res = {"value": round(S * args.steps / wall, 1), "unit": "tok/s", "ms_per_step": round(wall / args.steps * 1e3, 3),
+           "config": {"workload": "llama3-8b-layer: one Llama-3-8B-shaped decoder layer, bf16 weights, "
+                                  "x ~ N(0,1) bf16 [2048, 4096], positions 0..2047", "seq_len": S, "batch": 1,
+                      "parallelism": "none (1 GPU)"},
+           "prefill_tok_s": round(S / (layer_ms * 1e-3), 1), "layer_ms": round(layer_ms, 4),
+           "layer_mfma_frac": round((lin + att) / (layer_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+           "roofline": mfma_roofline("gate-up GEMM (M=2048, N=28672, K=4096) + SwiGLU", 2.0 * S * 2 * F * dim,
+                                     avg_ms(kt, "gate_up")),
+           "roofline_attention": mfma_roofline("causal GQA prefill attention (S=2048)", att, avg_ms(kt, "attn")),
+           "per_kernel": per_kernel_table(kt, "layer")}
+    if not args.no_cpu_baseline:
+        from oracle import decoder_layer
+        lw = {"attention_norm": host_w["layers.0.attention_norm.weight"], "wq": host_w["layers.0.attention.wq.weight"],
+              "wk": host_w["layers.0.attention.wk.weight"], "wv": host_w["layers.0.attention.wv.weight"],
+              "wo": host_w["layers.0.attention.wo.weight"], "ffn_norm": host_w["layers.0.ffn_norm.weight"],
+              "w1": host_w["layers.0.feed_forward.w1.weight"], "w3": host_w["layers.0.feed_forward.w3.weight"],
+              "w2": host_w["layers.0.feed_forward.w2.weight"]}
+        xs = x0.cpu().numpy()
+        ck = np.zeros((S, shape.n_kv_heads, shape.head_dim), np.float32)
+        cv = np.zeros_like(ck)
+        t0 = time.perf_counter()
+        decoder_layer(xs, lw, oracle_cfg(shape, 1), ck, cv, np.arange(S))
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(S / t, 2), "unit": "tok/s", "cores": blas_threads(), "kind": "oracle",
+                               "sample": "the whole workload: oracle decoder layer (numpy fp32 matmuls, fp64 "
+                                         "norms/softmax) on the same x, S=2048", "sample_seconds": round(t, 2)}
+    return res
+
+
+def bench_long_prefill(args, torch, B, inputs, LlamaModel) -> dict:
+    wl = inputs.WORKLOADS["llama3-8b-long-prefill"]
+    shape = wl.shape
+    S = wl.prompt_len
+    n_cpu = 0 if args.no_cpu_baseline else 2
+    dw, host_w = make_weights(shape, n_cpu, keep_head=not args.no_cpu_baseline)
+    model = LlamaModel(shape, dw, max_batch=1, max_prefill_tokens=S)
+    del dw
+    torch.cuda.empty_cache()
+    prompt_np = inputs.token_ids(shape.vocab_size, S)
+    prompt = torch.as_tensor(prompt_np, device="cuda:0")
+    logits = torch.empty(shape.vocab_size, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    h = model.handle
+    wall = time_steps(torch, lambda: B.llm_prefill(h, 0, prompt, S, 0, logits, stream), args.steps, args.warmup)
+    kt = timed_groups(B, h, lambda: B.llm_prefill(h, 0, prompt, S, 0, logits, stream))
+    lin, att = layer_flops(shape, S)
+    total_flops = shape.n_layers * (lin + att) + 2.0 * shape.dim * shape.vocab_size
+    t_step = wall / args.steps
+    F, dim = shape.ffn_hidden_dim, shape.dim
+    res = {"value": round(S * args.steps / wall, 1), "unit": "tok/s", "ms_per_step": round(t_step * 1e3, 3),
+           "config": {"workload": "llama3-8b-long-prefill: 32-layer Llama-3-8B-shaped bf16 model, prefill of 8192 "
+                                  "ids, last-position logits", "seq_len": S, "batch": 1,
+                      "parallelism": "none (1 GPU)"},
+           "prefill_tok_s": round(S / t_step, 1),
+           "step_mfma_frac": round(total_flops / t_step / 1e12 / MFMA_PEAK_TFLOPS, 4),
+           "roofline": mfma_roofline("gate-up GEMM (M=8192, N=28672, K=4096) + SwiGLU", 2.0 * S * 2 * F * dim,
+                                     avg_ms(kt, "gate_up")),
+           "roofline_attention": mfma_roofline("causal GQA prefill attention (S=8192)", att, avg_ms(kt, "attn")),
+           "per_kernel": per_kernel_table(kt, "prefill")}
+    if not args.no_cpu_baseline:
+        from oracle import OracleModel
+        n = 1024
+        om = OracleModel(oracle_cfg(shape.replace(max_seq_len=n), n_cpu), host_w, dtype=np.float32)
+        cache = om.new_cache(n)
+        t0 = time.perf_counter()
+        om.hidden(om.embed(prompt_np[:n]), cache, np.arange(n))
+        t = time.perf_counter() - t0
+        lin_n, att_n = layer_flops(shape, n)
+        scale = (shape.n_layers * (lin + att)) / (n_cpu * (lin_n + att_n))
+        res["cpu_baseline"] = {"value": round(S / (t * scale), 3), "unit": "tok/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": (f"oracle prefill of the first {n} ids through {n_cpu} of 32 layers "
+                                          f"(numpy fp32 matmuls), scaled by the flop ratio {scale:.1f} to 8192 ids "
+                                          f"x 32 layers"), "sample_seconds": round(t, 2)}
+    return res
+
+
+def bench_batched_decode(args, torch, B, inputs, LlamaModel) -> dict:
+    from concurrent.futures import ThreadPoolExecutor
+    wl = inputs.WORKLOADS["llama3-8b-batched-decode"]
+    shape = wl.shape
+    Bn = wl.batch
+    lo, hi = wl.kv_len_range
+    n_cpu = 0 if args.no_cpu_baseline else 2
+    dw, host_w = make_weights(shape, n_cpu, keep_head=not args.no_cpu_baseline)
+    model = LlamaModel(shape, dw, max_batch=Bn, max_prefill_tokens=1)
+    del dw
+    torch.cuda.empty_cache()
+    lengths = inputs.kv_lengths(Bn, lo, hi)
+    kv = model.kv_cache_view()
+    G, hd = shape.n_kv_heads, shape.head_dim
+    t0 = time.perf_counter()
+    jobs = [(w, b, g) for w in (0, 1) for b in range(Bn) for g in range(G)]
+    for l in range(shape.n_layers):
+        def gen(job, l=l):
+            w, b, g = job
+            return job, inputs.kv_contents_bf16_bits(l, w, b, g, int(lengths[b]), hd)
+        with ThreadPoolExecutor(16) as ex:
+            for (w, b, g), blk in ex.map(gen, jobs):
+                kv[l, w, b, g, : lengths[b]] = torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16).to(
+                    "cuda:0").to(kv.dtype)
+    log(f"cache contents generated in {time.perf_counter() - t0:.1f}s")
+    toks = torch.as_tensor(inputs.token_ids(shape.vocab_size, Bn, sub=4), device="cuda:0")
+    slots = torch.arange(Bn, dtype=torch.int32, device="cuda:0")
+    pos = torch.as_tensor(lengths, device="cuda:0")
+    logits = torch.empty(Bn, shape.vocab_size, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    h = model.handle
+
+    def step():
+        B.llm_decode_step(h, Bn, slots, pos, toks, logits, stream)
+
+    wall = time_steps(torch, step, args.steps, args.warmup)
+    assert model.read_device_error() == 0
+    kt = timed_groups(B, h, step)
+    t_step = wall / args.steps
+    L, dim, F, V = shape.n_layers, shape.dim, shape.ffn_hidden_dim, shape.vocab_size
+    w_bytes = 2 * (L * (dim * (shape.n_heads + 2 * G) * hd + dim * shape.n_heads * hd + 3 * F * dim) + V * dim)
+    kv_bytes = L * G * hd * 2 * 2 * float(np.sum(lengths.astype(np.int64) + 1))
+    att_bytes_per_launch = kv_bytes / L
+    res = {"value": round(Bn * args.steps / wall, 1), "unit": "tok/s", "ms_per_step": round(t_step * 1e3, 3),
+           "config": {"workload": "llama3-8b-batched-decode: 32-layer Llama-3-8B-shaped bf16 model, one decode step "
+                                  "for 64 sequences with cached lengths U{1024..8192}", "batch": Bn,
+                      "parallelism": "none (1 GPU)"},
+           "decode_tok_s": round(Bn / t_step, 1),
+           "step_hbm_frac": round((w_bytes + kv_bytes) / t_step / 1e9 / HBM_PEAK_GBS, 4),
+           "step_bytes": int(w_bytes + kv_bytes),
+           "roofline": hbm_roofline("split-KV decode attention + combine (per layer, 64 rows)", att_bytes_per_launch,
+                                    avg_ms(kt, "attn")),
+           "per_kernel": per_kernel_table(kt, "decode")}
+    if not args.no_cpu_baseline:
+        from oracle import OracleModel
+        om = OracleModel(oracle_cfg(shape.replace(max_seq_len=hi + 1), n_cpu), host_w, dtype=np.float32)
+        b = int(np.argmax(lengths))
+        Lb = int(lengths[b])
+        cache = om.new_cache(Lb + 1)
+        for l in range(n_cpu):
+            for w in (0, 1):
+                blk = np.stack([inputs.kv_contents_bf16_bits(l, w, b, g, Lb, hd) for g in range(G)])
+                cache[l][w][:Lb] = inputs.bf16_bits_to_f32(blk).transpose(1, 0, 2)
+        t0 = time.perf_counter()
+        hdn = om.hidden(om.embed([int(toks[b])]), cache, np.array([Lb]))
+        t1 = time.perf_counter()
+        om.logits_of(hdn)
+        t2 = time.perf_counter()
+        mean_scale = float(np.mean(lengths + 1)) / (Lb + 1)
+        t_row = (t1 - t0) * (L / n_cpu) * (0.5 + 0.5 * mean_scale) + (t2 - t1)
+        res["cpu_baseline"] = {"value": round(1.0 / t_row, 4), "unit": "tok/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": (f"oracle decode of the longest row (L={Lb}) through {n_cpu} of 32 layers "
+                                          f"plus the LM head; layers scaled to 32 (attention part to the mean length)"
+                                          f"; rows are independent so one row's rate is the batch rate"),
+                               "sample_seconds": round(t2 - t0, 2)}
+    return res
+
+
+WORKLOAD_FUNS = {"llama3-8b": bench_generate, "llama3-8b-layer": bench_layer,
+                 "llama3-8b-long-prefill": bench_long_prefill, "llama3-8b-batched-decode": bench_batched_decode}
 
 
 def main() -> int:
@@ -107,8 +435,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama3-8b", choices=sorted(WORKLOAD_FUNS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=4, help="layers in the CPU oracle sample")
+    ap.add_argument("--cpu-layers", type=int, default=4, help="layers in the CPU oracle sample (llama3-8b)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -121,139 +450,13 @@ def main() -> int:
     from llama_decoder_transformer_amd import inputs
     from llama_decoder_transformer_amd.model import LlamaModel
 
-    wl = inputs.WORKLOADS["llama3-8b"]
-    shape = wl.shape
-    P, T = wl.prompt_len, wl.decode_steps
-    dev = "cuda:0"
-    t0 = time.perf_counter()
-    dw, host_w = make_weights(shape, 0 if args.no_cpu_baseline else args.cpu_layers)
-    log(f"weights generated and uploaded in {time.perf_counter() - t0:.1f}s")
-    model = LlamaModel(shape, dw, max_batch=1, max_prefill_tokens=P, device=dev)
-    del dw
-    torch.cuda.empty_cache()
-    log("model initialised")
-
-    prompt_np = inputs.token_ids(shape.vocab_size, P)
-    prompt = torch.as_tensor(prompt_np, device=dev)
-    slots = torch.zeros(1, dtype=torch.int32, device=dev)
-    pos = torch.zeros(1, dtype=torch.int32, device=dev)
-    tok = torch.zeros(1, dtype=torch.int32, device=dev)
-    logits1 = torch.empty(shape.vocab_size, dtype=torch.float32, device=dev)
-    logitsB = torch.empty(1, shape.vocab_size, dtype=torch.float32, device=dev)
-    out = torch.empty(T, 1, dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
-    h = model.handle
-
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        B.llm_prefill(h, 0, prompt, P, 0, logits1, stream)
-        B.llm_argmax(logits1, 1, shape.vocab_size, tok, stream)
-        if ev:
-            ev[1].record(stream)
-        pos.fill_(P)
-        B.llm_generate(h, 1, slots, pos, tok, T, out, logitsB, stream)
-        if ev:
-            ev[2].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    prefill_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    assert model.read_device_error() == 0
-    gen_tokens = out[:, 0].cpu().tolist()
-    log(f"timed {args.steps} steps in {wall:.3f}s: prefill {prefill_ms:.3f} ms, decode {decode_ms / T:.3f} ms/token")
-
-    # Per-kernel durations: one prefill and one decode block with the library's event brackets.
-    def timed_groups(fn):
-        B.llm_set_kernel_timing(h, True)
-        fn()
-        res = {name: B.llm_kernel_timing(h, k) for k, name in enumerate(B.KERNEL_GROUPS)}
-        B.llm_set_kernel_timing(h, False)
-        return res
-
-    kt_prefill = timed_groups(lambda: B.llm_prefill(h, 0, prompt, P, 0, logits1, stream))
-    torch.cuda.synchronize()
-    pos.fill_(P)
-
-    def dec():
-        B.llm_generate(h, 1, slots, pos, tok, T, out, logitsB, stream)
-
-    kt_decode = timed_groups(dec)
-    torch.cuda.synchronize()
-
-    L, dim, F, V = shape.n_layers, shape.dim, shape.ffn_hidden_dim, shape.vocab_size
-    n_up, ms_up = kt_decode["gate_up"]
-    up_avg_ms = ms_up / n_up
-    up_bytes = 2 * F * dim * 2 + 2 * dim * 4 + F * 2  # w1|w3 weights + fp32 x and norm weight in + SwiGLU row out
-    up_gbs = up_bytes / (up_avg_ms * 1e-3) / 1e9
-    n_pup, ms_pup = kt_prefill["gate_up"]
-    pup_avg_ms = ms_pup / n_pup
-    pup_flops = 2.0 * P * (2 * F) * dim
-    pup_tflops = pup_flops / (pup_avg_ms * 1e-3) / 1e12
-
-    per_kernel = {}
-    for name in B.KERNEL_GROUPS:
-        n1, m1 = kt_prefill[name]
-        n2, m2 = kt_decode[name]
-        per_kernel[name] = {"prefill_launches": n1, "prefill_avg_us": round(m1 / n1 * 1e3, 2) if n1 else None,
-                            "decode_launches": n2, "decode_avg_us": round(m2 / n2 * 1e3, 2) if n2 else None}
-
-    # Whole-step HBM bytes of one decode token (weights except the embedding table, + KV read/write).
-    hd = dim // shape.n_heads
-    kv_pos_bytes = L * shape.n_kv_heads * hd * 2 * 2
-    w_bytes = 2 * (L * (dim * (shape.n_heads + 2 * shape.n_kv_heads) * hd + dim * shape.n_heads * hd
-                        + 3 * F * dim) + V * dim)
-    mean_ctx = P + (T - 1) / 2.0 + 1
-    dec_bytes = w_bytes + kv_pos_bytes * mean_ctx
-    decode_tok_s = T / (decode_ms * 1e-3)
-    prefill_tok_s = P / (prefill_ms * 1e-3)
-    value = (P + T) * args.steps / wall
-
-    res = {
-        "metric": "prefill tok/s + decode tok/s at Llama-3-8B shape, % of MFMA/HBM roofline",
-        "value": round(value, 3),
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "llama3-8b: 32-layer Llama-3-8B-shaped bf16 model, batch 1, prefill of 512 ids "
-                               "then 256 greedy KV-cached decode steps",
-                   "prompt_len": P, "decode_steps": T, "batch": 1, "parallelism": "none (1 GPU)"},
-        "prefill_tok_s": round(prefill_tok_s, 1),
-        "decode_tok_s": round(decode_tok_s, 2),
-        "prefill_ms": round(prefill_ms, 3),
-        "decode_ms_per_token": round(decode_ms / T, 4),
-        "decode_step_hbm_frac": round(dec_bytes / (decode_ms / T * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "decode gate-up projection (w1|w3 GEMV + SwiGLU), M=1", "bound": "hbm",
-                     "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(up_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": up_bytes, "avg_launch_us": round(up_avg_ms * 1e3, 2)},
-        "roofline_prefill": {"kernel": "prefill gate-up GEMM (M=512, N=28672, K=4096) + SwiGLU", "bound": "mfma",
-                             "achieved": round(pup_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(pup_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "flops_per_launch": pup_flops, "avg_launch_us": round(pup_avg_ms * 1e3, 2)},
-        "per_kernel": per_kernel,
-        "generated_first_tokens": gen_tokens[:8],
-    }
-    if not args.no_cpu_baseline:
-        t0 = time.perf_counter()
-        res["cpu_baseline"] = cpu_baseline(shape, host_w, prompt_np, args.cpu_layers, 4, T)
-        log(f"cpu baseline took {time.perf_counter() - t0:.1f}s")
+    body = WORKLOAD_FUNS[args.workload](args, torch, B, inputs, LlamaModel)
+    res = {"metric": METRIC, "value": body.pop("value"), "unit": body.pop("unit"), "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": body.pop("ms_per_step"), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "dtype_note": "fp16 MFMA operands with fp32 accumulation; bf16 weights held exactly as fp16; fp32 residual",
+           "data": "synthetic", "config": body.pop("config")}
+    res.update(body)
     print(json.dumps(res), flush=True)
     return 0
 
