@@ -381,22 +381,45 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 // softmax max needs only two cross-lane steps and the scaled probabilities,
 // packed to fp16, are already the B operand of O^T += V^T P^T.  The k-order of
 // that second product is the permutation {4g..4g+3, 16+4g..16+4g+3} of each
-// 32-key slice that the first product leaves in lane group g; the V^T operand is
-// read from a transposed LDS copy of V in the same order.
+// 32-key slice that the first product leaves in lane group g.  V stays row-major
+// in LDS; the transposing LDS read (ds_read_b64_tr_b16: lane i of a 16-lane group
+// receives element i%4 of the 4-element reads of lanes i/4, 4+i/4, 8+i/4, 12+i/4)
+// turns two 8-byte reads per lane into exactly that V^T fragment.
+//
+// K/V tiles are double-buffered in LDS: the next tile's global loads are issued
+// into registers before the current tile's math, stored after it, and a single
+// barrier per tile separates the two buffers' uses.  The causal mask is applied
+// only on tiles that cross a wave's diagonal, and the running max is raised only
+// when a score exceeds it by more than 2^8 (the accumulators are rescaled then,
+// for the whole wave at once); between raises the probabilities stay below 256,
+// well inside fp16, and the normalised result is the same softmax.
 
 constexpr int PF_D = 128;
 constexpr int PF_KT = 64;
-constexpr int PF_KLD = PF_D + 8;   // Ks row: 272 bytes
-constexpr int PF_VLD = PF_KT + 8;  // Vt row: 144 bytes
+constexpr int PF_KLD = PF_D + 8;    // K row stride: 272 bytes (b128 fragment reads: 16 rows hit 64 distinct banks)
+constexpr int PF_VLD = PF_D + 16;   // V row stride: 288 bytes (transposing reads: 8 rows x 32 bytes, distinct banks)
+constexpr int PF_KTILE = PF_KT * PF_KLD;  // elements
+constexpr int PF_VTILE = PF_KT * PF_VLD;
+constexpr size_t PF_LDS_BYTES = 2 * (size_t)(PF_KTILE + PF_VTILE) * sizeof(f16_t);
+constexpr float PF_RESCALE_LOG2 = 8.0f;
+
+typedef short pf_v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) pf_v4i16 pf_lds_v4i16;
+
+__device__ __forceinline__ uint2 pf_read_tr(const f16_t* lds_elem) {
+  const pf_v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_v4i16*)(lds_elem));
+  return __builtin_bit_cast(uint2, v);
+}
 
 template <int HPW>
-__global__ void __launch_bounds__(256) attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc,
                                                            const f16_t* __restrict__ vc, int slot, int pos0, int S,
                                                            int H, int G, int max_seq, f16_t* __restrict__ out) {
   constexpr int QSUB = 4 / HPW;  // 32-query sub-blocks per workgroup
   constexpr int QB = 32 * QSUB;
-  __shared__ __attribute__((aligned(16))) f16_t Ks[PF_KT * PF_KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[PF_D * PF_VLD];
+  extern __shared__ __attribute__((aligned(16))) f16_t pf_smem[];
+  f16_t* const Ks0 = pf_smem;                 // [2][PF_KT][PF_KLD]
+  f16_t* const Vs0 = pf_smem + 2 * PF_KTILE;  // [2][PF_KT][PF_VLD]
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -429,118 +452,155 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(const f16_t* __restri
   for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
     for (int jq = 0; jq < 2; ++jq) o[mb][jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // mrow: running max in the scaled log2 domain; lrow: this lane's part of the running sum.
   float mrow[2] = {-1e30f, -1e30f}, lrow[2] = {0.f, 0.f};
 
   const size_t base = ((size_t)slot * G + g) * (size_t)max_seq * PF_D;
   const f16_t* kb = kc + base;
   const f16_t* vb = vc + base;
   const int ntiles = (kv_end + PF_KT - 1) / PF_KT;
-  const int wave_last_pos = pos0 + qw0 + 31;
+  const int wave_first_pos = pos0 + qw0;
+  const int wave_last_pos = wave_first_pos + 31;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * PF_KT;
-    __syncthreads();
-    // K tile: 16 lanes per key row (coalesced), straight copy.
+  // Tile copy: 16 lanes per key row, 4 rows of K and of V per thread; keys past kv_end read as zero.
+  u32x4_t kr[4], vr[4];
+  auto fetch = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + i * 256, key = idx >> 4, c = idx & 15;
-      u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (k0 + key < kv_end) raw = *reinterpret_cast<const u32x4_t*>(kb + (size_t)(k0 + key) * PF_D + c * 8);
-      *reinterpret_cast<u32x4_t*>(&Ks[key * PF_KLD + c * 8]) = raw;
+      kr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      vr[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (k0 + key < kv_end) {
+        kr[i] = *reinterpret_cast<const u32x4_t*>(kb + (size_t)(k0 + key) * PF_D + c * 8);
+        vr[i] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)(k0 + key) * PF_D + c * 8);
+      }
     }
-    // V tile, transposed to Vt[d][key]: consecutive lanes take consecutive keys.
+  };
+  auto stash = [&](int buf) {
+    f16_t* Ks = Ks0 + buf * PF_KTILE;
+    f16_t* Vs = Vs0 + buf * PF_VTILE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + i * 256, key = idx & 63, c = idx >> 6;
-      u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (k0 + key < kv_end) raw = *reinterpret_cast<const u32x4_t*>(vb + (size_t)(k0 + key) * PF_D + c * 8);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        Vt[(c * 8 + 2 * w) * PF_VLD + key] = (uint16_t)(raw[w] & 0xFFFFu);
-        Vt[(c * 8 + 2 * w + 1) * PF_VLD + key] = (uint16_t)(raw[w] >> 16);
-      }
+      const int idx = tid + i * 256, key = idx >> 4, c = idx & 15;
+      *reinterpret_cast<u32x4_t*>(&Ks[key * PF_KLD + c * 8]) = kr[i];
+      *reinterpret_cast<u32x4_t*>(&Vs[key * PF_VLD + c * 8]) = vr[i];
     }
-    __syncthreads();
-    if (k0 > wave_last_pos) continue;  // every key of this tile is in this wave's future
+  };
 
-    // S^T = K Q^T : st[kb][jq][r] = score(key k0 + 16 kb + 4 lg + r, query jq*16 + l16)
-    f32x4_t st[4][2];
-#pragma unroll
-    for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-      for (int jq = 0; jq < 2; ++jq) st[kb4][jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4) {
-        const f16x8_t kf = *reinterpret_cast<const f16x8_t*>(&Ks[(kb4 * 16 + l16) * PF_KLD + s4 * 32 + lg * 8]);
-#pragma unroll
-        for (int jq = 0; jq < 2; ++jq)
-          st[kb4][jq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[jq][s4], st[kb4][jq], 0, 0, 0);
-      }
-    }
+  fetch(0);
+  stash(0);
+  __syncthreads();
 
-    // Online softmax per query column.
-    f16x8_t pf[2][2];  // [jq][k-step of 32 keys]
-#pragma unroll
-    for (int jq = 0; jq < 2; ++jq) {
-      const int qpos = pos0 + qw0 + jq * 16 + l16;
-      float tmax = -INFINITY;
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * PF_KT;
+    const bool more = t + 1 < ntiles;
+    if (more) fetch(k0 + PF_KT);
+    const f16_t* Ks = Ks0 + (t & 1) * PF_KTILE;
+    const f16_t* Vs = Vs0 + (t & 1) * PF_VTILE;
+
+    if (k0 <= wave_last_pos) {  // otherwise every key of this tile is in this wave's future
+      // S^T = K Q^T : st[kb][jq][r] = score(key k0 + 16 kb + 4 lg + r, query jq*16 + l16)
+      f32x4_t st[4][2];
 #pragma unroll
       for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = k0 + kb4 * 16 + lg * 4 + r;
-          float v = st[kb4][jq][r] * scale;
-          if (key > qpos) v = -INFINITY;
-          st[kb4][jq][r] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(mrow[jq], tmax);
-      const float alpha = exp2f(mrow[jq] - mn);
-      mrow[jq] = mn;
-      float psum = 0.f;
-      uint32_t packed[2][4];
+        for (int jq = 0; jq < 2; ++jq) st[kb4][jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4) {
-        float p[4];
+      for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = exp2f(st[kb4][jq][r] - mn);
-          psum += p[r];
+        for (int kb4 = 0; kb4 < 4; ++kb4) {
+          const f16x8_t kf = *reinterpret_cast<const f16x8_t*>(&Ks[(kb4 * 16 + l16) * PF_KLD + s4 * 32 + lg * 8]);
+#pragma unroll
+          for (int jq = 0; jq < 2; ++jq)
+            st[kb4][jq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[jq][s4], st[kb4][jq], 0, 0, 0);
         }
-        // k-step kb4/2 holds blocks 2t (elements 0..3) and 2t+1 (elements 4..7).
-        const int ks = kb4 >> 1, half = (kb4 & 1) * 2;
-        packed[ks][half] = pack_f16x2(p[0], p[1]);
-        packed[ks][half + 1] = pack_f16x2(p[2], p[3]);
       }
-      lrow[jq] = lrow[jq] * alpha + psum;
+
+      // Causal mask, only on tiles that reach past this wave's first query.
+      if (k0 + PF_KT - 1 > wave_first_pos) {
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) o[mb][jq] *= alpha;
+        for (int jq = 0; jq < 2; ++jq) {
+          const int qpos = wave_first_pos + jq * 16 + l16;
+#pragma unroll
+          for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (k0 + kb4 * 16 + lg * 4 + r > qpos) st[kb4][jq][r] = -INFINITY;
+        }
+      }
+
+      // Online softmax per query column (raw scores; scale > 0 keeps the max).
+      float tmax[2];
+#pragma unroll
+      for (int jq = 0; jq < 2; ++jq) {
+        float m = st[0][jq][0];
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) m = fmaxf(m, st[kb4][jq][r]);
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        tmax[jq] = m * scale;
+      }
+      const bool raise = tmax[0] > mrow[0] + PF_RESCALE_LOG2 || tmax[1] > mrow[1] + PF_RESCALE_LOG2;
+      if (__any(raise)) {
+#pragma unroll
+        for (int jq = 0; jq < 2; ++jq) {
+          const float mn = fmaxf(mrow[jq], tmax[jq]);
+          const float alpha = exp2f(mrow[jq] - mn);
+          mrow[jq] = mn;
+          lrow[jq] *= alpha;
+#pragma unroll
+          for (int mb = 0; mb < 8; ++mb) o[mb][jq] *= alpha;
+        }
+      }
+      f16x8_t pf[2][2];  // [jq][k-step of 32 keys]
+#pragma unroll
+      for (int jq = 0; jq < 2; ++jq) {
+        const float mneg = -mrow[jq];
+        float psum = 0.f;
+        uint32_t packed[2][4];
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4) {
+          float p[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(fmaf(st[kb4][jq][r], scale, mneg));
+            psum += p[r];
+          }
+          // k-step kb4/2 holds blocks 2t (elements 0..3) and 2t+1 (elements 4..7).
+          const int ks = kb4 >> 1, half = (kb4 & 1) * 2;
+          packed[ks][half] = pack_f16x2(p[0], p[1]);
+          packed[ks][half + 1] = pack_f16x2(p[2], p[3]);
+        }
+        lrow[jq] += psum;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4_t u = {packed[ks][0], packed[ks][1], packed[ks][2], packed[ks][3]};
+          pf[jq][ks] = __builtin_bit_cast(f16x8_t, u);
+        }
+      }
+
+      // O^T += V^T P^T.  A operand row d = 16 mb + l16, k = keys {4 lg + j, 16 + 4 lg + j} of the 32-key step:
+      // this lane's transposing reads address key row 32 ks + 4 lg + l16/4 (and +16), columns 16 mb + 4 (l16%4)..+3.
+      const f16_t* vlane = Vs + (4 * lg + (l16 >> 2)) * PF_VLD + 4 * (l16 & 3);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        u32x4_t u = {packed[ks][0], packed[ks][1], packed[ks][2], packed[ks][3]};
-        pf[jq][ks] = __builtin_bit_cast(f16x8_t, u);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+          const uint2 lo = pf_read_tr(vlane + (32 * ks) * PF_VLD + 16 * mb);
+          const uint2 hi = pf_read_tr(vlane + (32 * ks + 16) * PF_VLD + 16 * mb);
+          const u32x4_t u = {lo.x, lo.y, hi.x, hi.y};
+          const f16x8_t vf = __builtin_bit_cast(f16x8_t, u);
+#pragma unroll
+          for (int jq = 0; jq < 2; ++jq)
+            o[mb][jq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[jq][ks], o[mb][jq], 0, 0, 0);
+        }
       }
     }
 
-    // O^T += V^T P^T
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const uint16_t* vrow = &Vt[(mb * 16 + l16) * PF_VLD + ks * 32 + lg * 4];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        u32x4_t u = {lo.x, lo.y, hi.x, hi.y};
-        const f16x8_t vf = __builtin_bit_cast(f16x8_t, u);
-#pragma unroll
-        for (int jq = 0; jq < 2; ++jq)
-          o[mb][jq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[jq][ks], o[mb][jq], 0, 0, 0);
-      }
-    }
+    if (more) stash((t + 1) & 1);
+    __syncthreads();
   }
 
   // Normalise and store: lane holds d = 16 mb + 4 lg + r of query jq*16 + l16.
@@ -570,6 +630,18 @@ bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads) {
   return hpg == 1 || hpg == 2 || hpg % 4 == 0;
 }
 
+template <int HPW>
+static void attn_prefill_launch(dim3 grid, hipStream_t s, const f16_t* q, const f16_t* k, const f16_t* v, int slot,
+                                int pos0, int n_tokens, int H, int G, int max_seq, f16_t* out) {
+  static bool attr = false;  // the double-buffered tiles exceed the default 64 KiB dynamic LDS limit
+  if (!attr) {
+    attr = true;
+    (void)hipFuncSetAttribute((const void*)attn_prefill_kernel<HPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)PF_LDS_BYTES);
+  }
+  attn_prefill_kernel<HPW><<<grid, 256, PF_LDS_BYTES, s>>>(q, k, v, slot, pos0, n_tokens, H, G, max_seq, out);
+}
+
 void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0, int n_tokens,
                          int n_heads, int n_kv_heads, int head_dim, int max_seq, void* out, hipStream_t s) {
   if (n_tokens <= 0) return;
@@ -583,11 +655,11 @@ void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache
   const f16_t* vv = (const f16_t*)v_cache;
   f16_t* oo = (f16_t*)out;
   if (hpw == 4)
-    attn_prefill_kernel<4><<<grid, 256, 0, s>>>(qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
+    attn_prefill_launch<4>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
   else if (hpw == 2)
-    attn_prefill_kernel<2><<<grid, 256, 0, s>>>(qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
+    attn_prefill_launch<2>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
   else
-    attn_prefill_kernel<1><<<grid, 256, 0, s>>>(qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
+    attn_prefill_launch<1>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
 }
 
 }  // namespace llm

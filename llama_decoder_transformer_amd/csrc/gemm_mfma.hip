@@ -235,7 +235,9 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
   const f16_t* a = (const f16_t*)A;
   const f16_t* w = (const f16_t*)W;
   auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  if (M > 128 && tiles(256, 256) >= 192)
+  // The q|k|v epilogue (RoPE table reads, cache addressing) does not fit the 256 x 256
+  // tile's registers (it spills), so that projection stays on 128 x 128 tiles.
+  if (M > 128 && ep.kind != EPI_QKV && tiles(256, 256) >= 192)
     gemm_dispatch<256, 256, 2, 4, 1, true>(a, w, M, N, K, ep, s);
   else if (M > 64 && tiles(128, 128) >= 256)
     gemm_dispatch<128, 128, 2, 2>(a, w, M, N, K, ep, s);
