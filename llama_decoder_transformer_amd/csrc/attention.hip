@@ -9,6 +9,8 @@
 // exponentials are exp2.
 //
 // Cache layout (per layer, per K/V): [slot][kv_head][max_seq][head_dim].
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -326,11 +328,20 @@ static bool dec_single_pass(int rows, int n_heads, int max_seq) {
   return max_seq <= 1024 && rows * n_heads <= 512;
 }
 
+static bool attn_decode_mfma(const f16_t* q, const f16_t* kc, const f16_t* vc, const int* row_pos,
+                             const int* row_slot, int pos0, int slot0, int rows, int H, int G, int max_seq,
+                             int n_slots, float* partial, f16_t* out, int* err, hipStream_t s);
+
 template <typename T, int D>
 static void attn_decode_dispatch(const T* q, const T* kc, const T* vc, const int* row_pos, const int* row_slot,
                                  int pos0, int slot0, int rows, int H, int G, int max_seq, int n_slots,
                                  float* partial, T* out, int* err, hipStream_t s) {
   const int hpg = H / G;
+  if constexpr (std::is_same<T, f16_t>::value && D == 128) {
+    if (attn_decode_mfma(q, kc, vc, row_pos, row_slot, pos0, slot0, rows, H, G, max_seq, n_slots, partial, out, err,
+                         s))
+      return;
+  }
   if (dec_single_pass(rows, H, max_seq)) {
     dim3 grid(1, H, rows);
     attn_decode_kernel<T, D, 1024, 1><<<grid, 1024, 0, s>>>(q, kc, vc, row_pos, row_slot, pos0, slot0, H, G, max_seq,
@@ -622,6 +633,227 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
   }
+}
+
+// ============================================================== MFMA decode
+//
+// Decode rows (one query per row) with the group's query heads as the columns of
+// the matrix-core products (up to 16 heads per KV head).  Grid (chunk, kv-head,
+// row); each of the 4 waves takes a contiguous quarter of the chunk's keys in
+// steps of 32.  Per step, S^T = K Q^T takes its K operand straight from global
+// memory (lane = key row l16, 16 bytes of d), the online softmax runs per head
+// column as in the prefill kernel, and O^T += V^T P^T reads V^T through the
+// transposing LDS read from a wave-private row-major copy of the step's V rows.
+// The next step's K and V rows are loaded while the current step is computed.
+// The waves are merged through LDS; a chunk writes its (acc, max, sum) partial
+// for attn_combine_kernel, or the output when the row has a single chunk.
+
+constexpr int DM_STEP = 32;  // keys per wave step
+constexpr int DM_MAXH = 16;  // query heads per KV head (MFMA columns)
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_decode_mfma_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, const f16_t* __restrict__ vc,
+                        const int* __restrict__ row_pos, const int* __restrict__ row_slot, int pos0, int slot0, int H,
+                        int G, int max_seq, int n_slots, int CH, int nchunks, float* __restrict__ partial,
+                        f16_t* __restrict__ out, int* err) {
+  constexpr int D = PF_D;
+  constexpr int VT = DM_STEP * PF_VLD;  // elements of one wave's V tile
+  // V tiles during the key loop; the wave merge reuses the same bytes afterwards.
+  __shared__ __attribute__((aligned(16))) f16_t s_v[4 * VT];
+  __shared__ float s_m[4][DM_MAXH], s_l[4][DM_MAXH];
+  static_assert(4 * DM_MAXH * D * sizeof(float) <= sizeof(s_v), "merge buffer does not fit");
+
+  const int chunk = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
+  const int hpg = H / G, h0 = g * hpg;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int pos = row_pos ? row_pos[row] : pos0 + row;
+  const int slot = row_slot ? row_slot[row] : slot0;
+  f16_t* orow = out + (size_t)row * H * D;
+  if (pos < 0 || pos >= max_seq || slot < 0 || slot >= n_slots) {
+    if (chunk == 0) {
+      for (int t = tid; t < hpg * D; t += 256) orow[(size_t)h0 * D + t] = (f16_t)0.f;
+      if (tid == 0) atomicOr(err, (pos < 0 || pos >= max_seq) ? 2 : 4);
+    }
+    return;
+  }
+  const int start = chunk * CH;
+  if (start > pos) return;
+  const int end = min(pos + 1, start + CH);
+  const int nvalid = pos / CH + 1;
+  const int quarter = CH / 4;
+  const int wbeg = start + wid * quarter;
+  const int wend = min(end, wbeg + quarter);
+  const int nsteps = wend > wbeg ? (wend - wbeg + DM_STEP - 1) / DM_STEP : 0;
+  const float scale = LOG2E_F / sqrtf((float)D);
+
+  // Q^T fragments (B operand): column = head l16 of the group, k = 32 s + 8 lg .. +7.
+  f16x8_t qf[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    u32x4_t raw = {0u, 0u, 0u, 0u};
+    if (l16 < hpg)
+      raw = *reinterpret_cast<const u32x4_t*>(q + (size_t)row * H * D + (size_t)(h0 + l16) * D + s4 * 32 + lg * 8);
+    qf[s4] = __builtin_bit_cast(f16x8_t, raw);
+  }
+
+  const size_t base = ((size_t)slot * G + g) * (size_t)max_seq * D;
+  const f16_t* kb = kc + base;
+  const f16_t* vb = vc + base;
+  f16_t* const Vw = s_v + wid * VT;
+
+  f32x4_t o[8];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrow = -1e30f, lrow = 0.f;
+
+  // Raw rows of one step: K as MFMA A operands (key k0 + 16 kb + l16, d = 32 s + 8 lg), V in
+  // copy order (key (lane + 64 i) / 16, 16-byte column (lane + 64 i) % 16).
+  u32x4_t kr[2][2][4], vr[2][8];
+  auto fetch = [&](int set, int k0) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int key = k0 + kb2 * 16 + l16;
+      const bool ok = key < wend;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        kr[set][kb2][s4] = u32x4_t{0u, 0u, 0u, 0u};
+        if (ok) kr[set][kb2][s4] = *reinterpret_cast<const u32x4_t*>(kb + (size_t)key * D + s4 * 32 + lg * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = lane + 64 * i, key = k0 + (idx >> 4), c = idx & 15;
+      vr[set][i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (key < wend) vr[set][i] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)key * D + c * 8);
+    }
+  };
+
+  auto step = [&](int set, int k0) {
+    // V rows of this step into the wave's tile (LDS operations of one wave complete in order,
+    // so the transposing reads below see these stores, and the next step's stores follow them).
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = lane + 64 * i;
+      *reinterpret_cast<u32x4_t*>(&Vw[(idx >> 4) * PF_VLD + (idx & 15) * 8]) = vr[set][i];
+    }
+    f32x4_t st[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      st[kb2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        st[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, kr[set][kb2][s4]), qf[s4],
+                                                         st[kb2], 0, 0, 0);
+    }
+    // st[kb][r] = score(key k0 + 16 kb + 4 lg + r, head l16); keys past wend are masked.
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (k0 + kb2 * 16 + lg * 4 + r >= wend) st[kb2][r] = -INFINITY;
+        tmax = fmaxf(tmax, st[kb2][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax *= scale;
+    if (__any(tmax > mrow + PF_RESCALE_LOG2)) {
+      const float mn = fmaxf(mrow, tmax);
+      const float alpha = exp2f(mrow - mn);
+      mrow = mn;
+      lrow *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) o[mb] *= alpha;
+    }
+    const float mneg = -mrow;
+    float p[2][4];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[kb2][r] = __builtin_amdgcn_exp2f(fmaf(st[kb2][r], scale, mneg));
+        lrow += p[kb2][r];
+      }
+    const u32x4_t pu = {pack_f16x2(p[0][0], p[0][1]), pack_f16x2(p[0][2], p[0][3]), pack_f16x2(p[1][0], p[1][1]),
+                        pack_f16x2(p[1][2], p[1][3])};
+    const f16x8_t pf = __builtin_bit_cast(f16x8_t, pu);
+    const f16_t* vlane = Vw + (4 * lg + (l16 >> 2)) * PF_VLD + 4 * (l16 & 3);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const uint2 lo = pf_read_tr(vlane + 16 * mb);
+      const uint2 hi = pf_read_tr(vlane + 16 * PF_VLD + 16 * mb);
+      const u32x4_t u = {lo.x, lo.y, hi.x, hi.y};
+      o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, u), pf, o[mb], 0, 0, 0);
+    }
+  };
+
+  if (nsteps > 0) fetch(0, wbeg);
+  for (int i = 0; i < nsteps; i += 2) {
+    const int k0 = wbeg + i * DM_STEP;
+    if (i + 1 < nsteps) fetch(1, k0 + DM_STEP);
+    step(0, k0);
+    if (i + 1 >= nsteps) break;
+    if (i + 2 < nsteps) fetch(0, k0 + 2 * DM_STEP);
+    step(1, k0 + DM_STEP);
+  }
+
+  // Merge the 4 waves: lane (l16, lg) holds head l16, d = 16 mb + 4 lg + r.
+  lrow += __shfl_xor(lrow, 16);
+  lrow += __shfl_xor(lrow, 32);
+  __syncthreads();  // every wave is done with its V tile
+  float* s_o = reinterpret_cast<float*>(s_v);  // [4][DM_MAXH][D]
+  if (l16 < hpg) {
+    if (lg == 0) { s_m[wid][l16] = mrow; s_l[wid][l16] = lrow; }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_o[((size_t)wid * DM_MAXH + l16) * D + mb * 16 + lg * 4 + r] = o[mb][r];
+  }
+  __syncthreads();
+  for (int t = tid; t < hpg * D; t += 256) {
+    const int hh = t / D, e = t % D;
+    float M = s_m[0][hh];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][hh]);
+    float L = 0.f, a = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = exp2f(s_m[w][hh] - M);
+      L += s_l[w][hh] * wt;
+      a += s_o[((size_t)w * DM_MAXH + hh) * D + e] * wt;
+    }
+    if (nvalid == 1) {
+      orow[(size_t)(h0 + hh) * D + e] = (f16_t)(a / L);
+    } else {
+      float* pr = partial + (((size_t)row * H + h0 + hh) * nchunks + chunk) * (D + 2);
+      pr[e] = a;
+      if (e == 0) { pr[D] = M; pr[D + 1] = L; }
+    }
+  }
+}
+
+// Chunk of the MFMA decode kernel: a multiple of 128 keys (4 waves x 32), halved from 2048
+// until rows x kv-heads x chunks reaches 2048 workgroups.
+static int dec_mfma_chunk(int rows, int n_kv_heads, int max_seq) {
+  int ch = 2048;
+  while (ch > 128 && (long)rows * n_kv_heads * ((max_seq + ch - 1) / ch) < 2048) ch >>= 1;
+  return ch;
+}
+
+static bool attn_decode_mfma(const f16_t* q, const f16_t* kc, const f16_t* vc, const int* row_pos,
+                             const int* row_slot, int pos0, int slot0, int rows, int H, int G, int max_seq,
+                             int n_slots, float* partial, f16_t* out, int* err, hipStream_t s) {
+  const int hpg = H / G;
+  if (hpg > DM_MAXH) return false;
+  const int CH = dec_mfma_chunk(rows, G, max_seq);
+  const int nch = (max_seq + CH - 1) / CH;
+  attn_decode_mfma_kernel<<<dim3(nch, G, rows), 256, 0, s>>>(q, kc, vc, row_pos, row_slot, pos0, slot0, H, G, max_seq,
+                                                             n_slots, CH, nch, partial, out, err);
+  if (nch > 1)
+    attn_combine_kernel<f16_t, PF_D><<<dim3(H, rows), 128, nch * sizeof(float), s>>>(
+        partial, row_pos, row_slot, pos0, slot0, H, max_seq, n_slots, CH, nch, out);
+  return true;
 }
 
 bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads) {

@@ -22,6 +22,8 @@
 // index is remapped so that each XCD receives a contiguous run of tiles, ordered
 // N-tile-major: the M tiles that share a weight tile run on the same XCD (one L2)
 // at about the same time and the weights are fetched from HBM once.
+#include <algorithm>
+
 #include "common.h"
 #include "epilogue.h"
 #include "launch.h"
@@ -40,7 +42,8 @@ __device__ __forceinline__ int lds_off(int r, int c) { return r * GEMM_LDK + ((c
 template <int BM, int BN, int WGM, int WGN, int EPI, int NPART = 1, bool SB = false>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* __restrict__ A,
                                                                   const f16_t* __restrict__ W, int M, int N, int K,
-                                                                  int tiles_m, int tiles_n, EpiParams ep) {
+                                                                  int tiles_m, int tiles_n, EpiParams ep,
+                                                                  int kb_per) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int BK = GEMM_BK, LDK = GEMM_LDK;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -116,10 +119,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
 #pragma unroll
     for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (K + BK - 1) / BK;
+  // K range of this workgroup: kb_per steps of BK starting at split blockIdx.y.
+  const int kb0 = blockIdx.y * kb_per;
+  const int nk = min(kb_per, (K + BK - 1) / BK - kb0);
+  const int kbase = kb0 * BK;
 #pragma unroll
   for (int part = 0; part < NPART; ++part) {
-    gload(0, part);
+    gload(kbase, part);
     sstore(0, part);
   }
   __syncthreads();
@@ -131,7 +137,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       constexpr int KS_PER_PART = (BK / 32) / NPART;
-      if (more && ks % KS_PER_PART == 0) gload((kt + 1) * BK, ks / KS_PER_PART);
+      if (more && ks % KS_PER_PART == 0) gload(kbase + (kt + 1) * BK, ks / KS_PER_PART);
       f16x8_t af[FM], bw[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -152,7 +158,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
     __syncthreads();
   }
 
-  // Epilogue.
+  // Epilogue.  A split-K workgroup stores its partial sums to slice blockIdx.y.
+  float* const out_f32 = ep.out_f32 + (size_t)blockIdx.y * M * ep.ld;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -169,8 +176,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
             else if ((n & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
           }
         } else if (m < M && n < N) {
-          if (EPI == EPI_STORE_F32) ep.out_f32[(size_t)m * ep.ld + n] = v;
-          else ep.out_f32[(size_t)m * ep.ld + n] += v;
+          if (EPI == EPI_STORE_F32) out_f32[(size_t)m * ep.ld + n] = v;
+          else out_f32[(size_t)m * ep.ld + n] += v;
         }
       }
     }
@@ -183,23 +190,26 @@ static size_t gemm_lds_bytes() {
 }
 
 template <int BM, int BN, int WGM, int WGN, int NPART = 1, bool SB = false>
-static void gemm_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep, hipStream_t s) {
+static void gemm_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep, hipStream_t s,
+                          int splits = 1) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  const dim3 grid(tm * tn);
+  const int nkb = (K + GEMM_BK - 1) / GEMM_BK;
+  const int kb_per = (nkb + splits - 1) / splits;
+  const dim3 grid(tm * tn, (nkb + kb_per - 1) / kb_per);
   const int nt = 64 * WGM * WGN;
   const size_t lds = gemm_lds_bytes<BM, BN>();
   switch (ep.kind) {
     case EPI_STORE_F32:
-      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_STORE_F32, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep);
+      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_STORE_F32, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_RESID:
-      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_RESID, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep);
+      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_RESID, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_QKV:
-      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_QKV, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep);
+      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_QKV, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_SWIGLU:
-      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_SWIGLU, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep);
+      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_SWIGLU, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep, kb_per);
       break;
   }
 }
@@ -229,12 +239,80 @@ static void gemm_init_attributes() {
 // Tile choice from a sweep of the Llama-3-8B projection shapes at M = 512, 2048
 // and 8192 on MI355X: the 8-wave 256 x 256 tile when it still yields at least 192
 // tiles, then 128 x 128 with at least 256 tiles (one per CU), else 64 x 64.
-void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep, hipStream_t s) {
+// Split-K second pass: out = epilogue(sum over the splits of part[s][m][n]), summed in split
+// order.  One thread per 4 consecutive columns (N % 4 == 0), so RoPE partners (2j, 2j+1)
+// and SwiGLU gate/up pairs (2c, 2c+1) are in the same thread.
+template <int EPI>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                                            EpiParams ep) {
+  const size_t i4 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t slice = (size_t)M * N;
+  if (i4 * 4 >= slice) return;
+  const size_t e = i4 * 4;
+  const int m = (int)(e / N), n = (int)(e % N);
+  float4 v = *reinterpret_cast<const float4*>(part + e);
+  for (int sp = 1; sp < splits; ++sp) {
+    const float4 w = *reinterpret_cast<const float4*>(part + (size_t)sp * slice + e);
+    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  }
+  const float a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (EPI == EPI_STORE_F32) ep.out_f32[(size_t)m * ep.ld + n + c] = a[c];
+    else if (EPI == EPI_RESID) ep.out_f32[(size_t)m * ep.ld + n + c] += a[c];
+    else if (EPI == EPI_QKV) epi_qkv<f16_t>(ep, m, n + c, a[c], a[c ^ 1]);
+    else if ((c & 1) == 0) epi_swiglu<f16_t>(ep, m, (n + c) >> 1, a[c], a[c + 1]);
+  }
+}
+
+// Number of K splits for a GEMM: only small-M shapes whose 64 x 64 tiles cannot fill the
+// GPU (fewer than 384 tiles) are split, aiming at about 512 workgroups, at most 8 splits
+// and at least 4 K steps of 64 per split.
+int gemm_splitk_count(int M, int N, int K) {
+  if (M <= 0 || M > 128 || N % 4 != 0) return 1;
+  const long tiles = (long)((M + 63) / 64) * ((N + 63) / 64);
+  if (tiles >= 384) return 1;
+  const int nkb = (K + GEMM_BK - 1) / GEMM_BK;
+  int sp = (int)std::min<long>(8, (512 + tiles - 1) / tiles);
+  sp = std::min(sp, nkb / 4);
+  if (sp < 2) return 1;
+  const int per = (nkb + sp - 1) / sp;
+  return (nkb + per - 1) / per;
+}
+
+size_t gemm_splitk_floats(int M, int N, int K) {
+  const int sp = gemm_splitk_count(M, N, K);
+  return sp > 1 ? (size_t)sp * M * N : 0;
+}
+
+// Tile choice from a sweep of the Llama-3-8B projection shapes at M = 512, 2048
+// and 8192 on MI355X: the 8-wave 256 x 256 tile when it still yields at least 192
+// tiles, then 128 x 128 with at least 256 tiles (one per CU), else 64 x 64, split
+// over K when even those are too few.
+void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep, float* splitk_ws,
+                     size_t splitk_ws_floats, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
   gemm_init_attributes();
   const f16_t* a = (const f16_t*)A;
   const f16_t* w = (const f16_t*)W;
   auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  const int sp = gemm_splitk_count(M, N, K);
+  if (sp > 1 && splitk_ws && (size_t)sp * M * N <= splitk_ws_floats) {
+    EpiParams pe = ep;
+    pe.kind = EPI_STORE_F32;
+    pe.out_f32 = splitk_ws;
+    pe.ld = N;
+    gemm_dispatch<64, 64, 2, 2>(a, w, M, N, K, pe, s, sp);
+    const size_t n4 = (size_t)M * N / 4;
+    const dim3 grid((unsigned)((n4 + 255) / 256));
+    switch (ep.kind) {
+      case EPI_STORE_F32: splitk_reduce_kernel<EPI_STORE_F32><<<grid, 256, 0, s>>>(splitk_ws, sp, M, N, ep); break;
+      case EPI_RESID: splitk_reduce_kernel<EPI_RESID><<<grid, 256, 0, s>>>(splitk_ws, sp, M, N, ep); break;
+      case EPI_QKV: splitk_reduce_kernel<EPI_QKV><<<grid, 256, 0, s>>>(splitk_ws, sp, M, N, ep); break;
+      case EPI_SWIGLU: splitk_reduce_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(splitk_ws, sp, M, N, ep); break;
+    }
+    return;
+  }
   // The q|k|v epilogue (RoPE table reads, cache addressing) does not fit the 256 x 256
   // tile's registers (it spills), so that projection stays on 128 x 128 tiles.
   if (M > 128 && ep.kind != EPI_QKV && tiles(256, 256) >= 192)

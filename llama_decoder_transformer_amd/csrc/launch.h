@@ -52,9 +52,15 @@ void launch_advance(int* positions, const int* tokens, int* out_tokens, int* ste
                     hipStream_t s);
 
 // Projections.
-// fp16 MFMA GEMM for M > 8 (A fp16 [M][K], W fp16 [N][K], fp32 accumulation).
-void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep,
-                      hipStream_t s);
+// fp16 MFMA GEMM for M > 8 (A fp16 [M][K], W fp16 [N][K], fp32 accumulation).  Shapes with
+// too few output tiles to fill the GPU (small M) split K over several workgroups: fp32
+// partials go to `splitk_ws` (gemm_splitk_floats(M, N, K) floats) and a second pass sums
+// them in a fixed order and applies the epilogue.  Without enough workspace the GEMM runs
+// unsplit.
+int gemm_splitk_count(int M, int N, int K);
+size_t gemm_splitk_floats(int M, int N, int K);
+void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep, float* splitk_ws,
+                     size_t splitk_ws_floats, hipStream_t s);
 // Vector GEMV for small M.  With norm_w == nullptr, A has the activation dtype; otherwise A
 // is the fp32 residual stream and the RMSNorm (weight norm_w, eps) is fused into the pass.
 void launch_gemv(int dtype, const void* A, const void* W, const float* norm_w, float eps, int M, int N, int K,

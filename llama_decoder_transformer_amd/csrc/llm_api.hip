@@ -1,5 +1,6 @@
 // C ABI of the decoder pass: validation, weight packing, buffer layout and the
 // per-layer launch sequence.  Declarations and contracts live in include/llm.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -84,7 +85,7 @@ struct PackedLayout {
 
 // Workspace layout.
 struct WorkLayout {
-  size_t flags, x, a, q, o, u, attn, amax, total;
+  size_t flags, x, a, q, o, u, attn, amax, splitk, splitk_floats, total;
   explicit WorkLayout(const llm_config& c) {
     Dims d(c);
     const size_t R = (size_t)d.rows();
@@ -99,6 +100,14 @@ struct WorkLayout {
     u = p; p = align256(p + R * d.F * d.es);
     attn = p; p = align256(p + attn_decode_partial_floats(att_rows, d.H, d.hd, d.S) * 4);
     amax = p; p = align256(p + (size_t)d.B * argmax_blocks(d.V) * 8);
+    // split-K partials of the MFMA projections at small row counts
+    splitk_floats = 0;
+    if (c.dtype == LLM_BF16) {
+      const int shapes[4][2] = {{d.qkv_rows(), d.dim}, {d.dim, d.H * d.hd}, {2 * d.F, d.dim}, {d.dim, d.F}};
+      for (int M = 9; M <= (int)std::min<size_t>(R, 128); ++M)
+        for (auto& sh : shapes) splitk_floats = std::max(splitk_floats, gemm_splitk_floats(M, sh[0], sh[1]));
+    }
+    splitk = p; p = align256(p + splitk_floats * 4);
     total = p;
   }
 };
@@ -146,6 +155,8 @@ struct llm_model {
   void* u;
   float* attn;
   void* amax;
+  float* splitk;
+  size_t splitk_floats;
   bool mfma_prefill;
   hipStream_t cap_stream;
   std::vector<GraphEntry> graphs;
@@ -239,7 +250,7 @@ void project(llm_model* m, const void* A, const void* W, int M, int N, int K, co
       launch_rmsnorm(c.dtype, (const float*)A, norm_w, M, K, c.norm_eps, m->a, s);
       A = m->a;
     }
-    launch_gemm_f16(A, W, M, N, K, ep, s);
+    launch_gemm_f16(A, W, M, N, K, ep, m->splitk, m->splitk_floats, s);
   } else {
     launch_gemv(c.dtype, A, W, norm_w, c.norm_eps, M, N, K, ep, s);
   }
@@ -401,6 +412,8 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   m->u = ws + wl.u;
   m->attn = (float*)(ws + wl.attn);
   m->amax = ws + wl.amax;
+  m->splitk = (float*)(ws + wl.splitk);
+  m->splitk_floats = wl.splitk_floats;
   m->mfma_prefill = c.dtype == LLM_BF16 && attn_prefill_supported(d.hd, d.H, d.G);
   m->cap_stream = nullptr;
 
