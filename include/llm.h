@@ -204,12 +204,16 @@ llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev,
 llm_status llm_read_device_error(llm_model* m, int32_t* flags, void* stream);
 
 /*
- * Kernel timing (diagnostics).  While enabled, each kernel group the library
- * launches directly on a stream is bracketed by two hipEvents recorded on that
- * stream (llm_generate then launches directly instead of replaying its graph).
- * Enabling resets the totals.  llm_kernel_timing synchronises on the recorded
- * events and returns, for one LLM_K_* group, the number of bracketed launches
- * and their summed duration in milliseconds.  Errors: INVALID_ARG, HIP.
+ * Kernel timing (diagnostics).  While enabled, every kernel the library
+ * launches directly records a start and a stop hipEvent with its own dispatch
+ * (hipExtLaunchKernelGGL), so the measured span is the kernel's execution and
+ * excludes queueing and launch gaps; llm_generate then launches directly
+ * instead of replaying its graph.  Kernels are charged to LLM_K_* groups (one
+ * group invocation may launch several kernels, e.g. a split-K GEMM and its
+ * reduce pass).  Enabling resets the totals.  llm_kernel_timing synchronises on
+ * the recorded events and returns, for one group, the number of invocations
+ * and the summed kernel execution time in milliseconds.  Errors: INVALID_ARG,
+ * HIP.
  */
 enum {
   LLM_K_EMBED = 0, LLM_K_RMSNORM = 1, LLM_K_QKV = 2, LLM_K_ATTN = 3, LLM_K_WO = 4,

@@ -344,7 +344,7 @@ static void attn_decode_dispatch(const T* q, const T* kc, const T* vc, const int
   }
   if (dec_single_pass(rows, H, max_seq)) {
     dim3 grid(1, H, rows);
-    attn_decode_kernel<T, D, 1024, 1><<<grid, 1024, 0, s>>>(q, kc, vc, row_pos, row_slot, pos0, slot0, H, G, max_seq,
+    launch_k(attn_decode_kernel<T, D, 1024, 1>, grid, 1024, 0, s, q, kc, vc, row_pos, row_slot, pos0, slot0, H, G, max_seq,
                                                            n_slots, max_seq, 1, 1, partial, out, err);
     return;
   }
@@ -352,10 +352,10 @@ static void attn_decode_dispatch(const T* q, const T* kc, const T* vc, const int
   const int nch = (max_seq + CH - 1) / CH;
   const int hpb = dec_hpb(H, G);
   dim3 grid(nch, G * (hpg / hpb), rows);
-  attn_decode_kernel<T, D, 256, DEC_MAXH><<<grid, 256, 0, s>>>(q, kc, vc, row_pos, row_slot, pos0, slot0, H, G,
+  launch_k(attn_decode_kernel<T, D, 256, DEC_MAXH>, grid, 256, 0, s, q, kc, vc, row_pos, row_slot, pos0, slot0, H, G,
                                                               max_seq, n_slots, CH, nch, hpb, partial, out, err);
   if (nch > 1)
-    attn_combine_kernel<T, D><<<dim3(H, rows), 128, nch * sizeof(float), s>>>(partial, row_pos, row_slot, pos0, slot0,
+    launch_k(attn_combine_kernel<T, D>, dim3(H, rows), 128, nch * sizeof(float), s, partial, row_pos, row_slot, pos0, slot0,
                                                                             H, max_seq, n_slots, CH, nch, out);
 }
 
@@ -651,17 +651,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 constexpr int DM_STEP = 32;  // keys per wave step
 constexpr int DM_MAXH = 16;  // query heads per KV head (MFMA columns)
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_decode_mfma_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, const f16_t* __restrict__ vc,
                         const int* __restrict__ row_pos, const int* __restrict__ row_slot, int pos0, int slot0, int H,
                         int G, int max_seq, int n_slots, int CH, int nchunks, float* __restrict__ partial,
                         f16_t* __restrict__ out, int* err) {
   constexpr int D = PF_D;
+  constexpr int NT = 64 * NW;
   constexpr int VT = DM_STEP * PF_VLD;  // elements of one wave's V tile
   // V tiles during the key loop; the wave merge reuses the same bytes afterwards.
-  __shared__ __attribute__((aligned(16))) f16_t s_v[4 * VT];
-  __shared__ float s_m[4][DM_MAXH], s_l[4][DM_MAXH];
-  static_assert(4 * DM_MAXH * D * sizeof(float) <= sizeof(s_v), "merge buffer does not fit");
+  __shared__ __attribute__((aligned(16))) f16_t s_v[NW * VT];
+  __shared__ float s_m[NW][DM_MAXH], s_l[NW][DM_MAXH];
+  static_assert(NW * DM_MAXH * D * sizeof(float) <= sizeof(s_v), "merge buffer does not fit");
 
   const int chunk = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
   const int hpg = H / G, h0 = g * hpg;
@@ -672,7 +674,7 @@ attn_decode_mfma_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ k
   f16_t* orow = out + (size_t)row * H * D;
   if (pos < 0 || pos >= max_seq || slot < 0 || slot >= n_slots) {
     if (chunk == 0) {
-      for (int t = tid; t < hpg * D; t += 256) orow[(size_t)h0 * D + t] = (f16_t)0.f;
+      for (int t = tid; t < hpg * D; t += NT) orow[(size_t)h0 * D + t] = (f16_t)0.f;
       if (tid == 0) atomicOr(err, (pos < 0 || pos >= max_seq) ? 2 : 4);
     }
     return;
@@ -681,7 +683,7 @@ attn_decode_mfma_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ k
   if (start > pos) return;
   const int end = min(pos + 1, start + CH);
   const int nvalid = pos / CH + 1;
-  const int quarter = CH / 4;
+  const int quarter = CH / NW;
   const int wbeg = start + wid * quarter;
   const int wend = min(end, wbeg + quarter);
   const int nsteps = wend > wbeg ? (wend - wbeg + DM_STEP - 1) / DM_STEP : 0;
@@ -802,7 +804,7 @@ attn_decode_mfma_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ k
   lrow += __shfl_xor(lrow, 16);
   lrow += __shfl_xor(lrow, 32);
   __syncthreads();  // every wave is done with its V tile
-  float* s_o = reinterpret_cast<float*>(s_v);  // [4][DM_MAXH][D]
+  float* s_o = reinterpret_cast<float*>(s_v);  // [NW][DM_MAXH][D]
   if (l16 < hpg) {
     if (lg == 0) { s_m[wid][l16] = mrow; s_l[wid][l16] = lrow; }
 #pragma unroll
@@ -811,14 +813,14 @@ attn_decode_mfma_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ k
       for (int r = 0; r < 4; ++r) s_o[((size_t)wid * DM_MAXH + l16) * D + mb * 16 + lg * 4 + r] = o[mb][r];
   }
   __syncthreads();
-  for (int t = tid; t < hpg * D; t += 256) {
+  for (int t = tid; t < hpg * D; t += NT) {
     const int hh = t / D, e = t % D;
     float M = s_m[0][hh];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][hh]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][hh]);
     float L = 0.f, a = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float wt = exp2f(s_m[w][hh] - M);
       L += s_l[w][hh] * wt;
       a += s_o[((size_t)w * DM_MAXH + hh) * D + e] * wt;
@@ -848,10 +850,10 @@ static bool attn_decode_mfma(const f16_t* q, const f16_t* kc, const f16_t* vc, c
   if (hpg > DM_MAXH) return false;
   const int CH = dec_mfma_chunk(rows, G, max_seq);
   const int nch = (max_seq + CH - 1) / CH;
-  attn_decode_mfma_kernel<<<dim3(nch, G, rows), 256, 0, s>>>(q, kc, vc, row_pos, row_slot, pos0, slot0, H, G, max_seq,
+  launch_k(attn_decode_mfma_kernel<4>, dim3(nch, G, rows), 256, 0, s, q, kc, vc, row_pos, row_slot, pos0, slot0, H, G, max_seq,
                                                              n_slots, CH, nch, partial, out, err);
   if (nch > 1)
-    attn_combine_kernel<f16_t, PF_D><<<dim3(H, rows), 128, nch * sizeof(float), s>>>(
+    launch_k(attn_combine_kernel<f16_t, PF_D>, dim3(H, rows), 128, nch * sizeof(float), s, 
         partial, row_pos, row_slot, pos0, slot0, H, max_seq, n_slots, CH, nch, out);
   return true;
 }
@@ -871,7 +873,7 @@ static void attn_prefill_launch(dim3 grid, hipStream_t s, const f16_t* q, const 
     (void)hipFuncSetAttribute((const void*)attn_prefill_kernel<HPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)PF_LDS_BYTES);
   }
-  attn_prefill_kernel<HPW><<<grid, 256, PF_LDS_BYTES, s>>>(q, k, v, slot, pos0, n_tokens, H, G, max_seq, out);
+  launch_k(attn_prefill_kernel<HPW>, grid, 256, PF_LDS_BYTES, s, q, k, v, slot, pos0, n_tokens, H, G, max_seq, out);
 }
 
 void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0, int n_tokens,

@@ -1,4 +1,6 @@
 // Embedding gather, RMSNorm, greedy argmax and small bookkeeping kernels.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -29,9 +31,9 @@ void launch_embed(int dtype, const void* emb, const int* tokens, int M, int dim,
                   int* err, hipStream_t s) {
   if (M <= 0) return;
   if (dtype == 1)
-    embed_kernel<f16_t><<<M, 256, 0, s>>>((const f16_t*)emb, tokens, dim, vocab, x, err);
+    launch_k(embed_kernel<f16_t>, M, 256, 0, s, (const f16_t*)emb, tokens, dim, vocab, x, err);
   else
-    embed_kernel<float><<<M, 256, 0, s>>>((const float*)emb, tokens, dim, vocab, x, err);
+    launch_k(embed_kernel<float>, M, 256, 0, s, (const float*)emb, tokens, dim, vocab, x, err);
 }
 
 // ---------------------------------------------------------------- RMSNorm
@@ -69,9 +71,9 @@ void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, f
                     hipStream_t s) {
   if (M <= 0) return;
   if (dtype == 1)
-    rmsnorm_kernel<f16_t><<<M, 256, 0, s>>>(x, w, dim, eps, (f16_t*)out);
+    launch_k(rmsnorm_kernel<f16_t>, M, 256, 0, s, x, w, dim, eps, (f16_t*)out);
   else
-    rmsnorm_kernel<float><<<M, 256, 0, s>>>(x, w, dim, eps, (float*)out);
+    launch_k(rmsnorm_kernel<float>, M, 256, 0, s, x, w, dim, eps, (float*)out);
 }
 
 // ---------------------------------------------------------------- small helpers
@@ -85,9 +87,9 @@ void launch_to_f32(int dtype, const void* src, float* dst, size_t n, hipStream_t
   if (n == 0) return;
   unsigned g = (unsigned)((n + 255) / 256);
   if (dtype == 1)
-    to_f32_kernel<bf16_t><<<g, 256, 0, s>>>((const bf16_t*)src, dst, n);
+    launch_k(to_f32_kernel<bf16_t>, g, 256, 0, s, (const bf16_t*)src, dst, n);
   else
-    to_f32_kernel<float><<<g, 256, 0, s>>>((const float*)src, dst, n);
+    launch_k(to_f32_kernel<float>, g, 256, 0, s, (const float*)src, dst, n);
 }
 
 // Weight packing for the bf16-weight path: rows of a bf16 matrix are widened and
@@ -95,17 +97,18 @@ void launch_to_f32(int dtype, const void* src, float* dst, size_t n, hipStream_t
 // magnitude lies in fp16's normal range) at destination row r * row_mult + row_off.
 __global__ void pack_rows_kernel(const bf16_t* __restrict__ src, f16_t* __restrict__ dst, size_t rows, int cols,
                                  int row_mult, int row_off) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= rows * (size_t)cols) return;
-  const size_t r = i / cols, c = i % cols;
-  dst[(r * row_mult + row_off) * (size_t)cols + c] = (f16_t)bf16_to_f32(src[i]);
+  const size_t n = rows * (size_t)cols;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / cols, c = i % cols;
+    dst[(r * row_mult + row_off) * (size_t)cols + c] = (f16_t)bf16_to_f32(src[i]);
+  }
 }
 
 void launch_pack_rows(const void* src, void* dst, size_t rows, int cols, int row_mult, int row_off, hipStream_t s) {
   const size_t n = rows * (size_t)cols;
   if (n == 0) return;
-  pack_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>((const bf16_t*)src, (f16_t*)dst, rows, cols, row_mult,
-                                                               row_off);
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 16384);  // grid-stride beyond 4M elements
+  launch_k(pack_rows_kernel, blocks, 256, 0, s, (const bf16_t*)src, (f16_t*)dst, rows, cols, row_mult, row_off);
 }
 
 __global__ void fill_i32_kernel(int* p, int v, size_t n) {
@@ -115,7 +118,7 @@ __global__ void fill_i32_kernel(int* p, int v, size_t n) {
 
 void launch_fill_i32(int* p, int v, size_t n, hipStream_t s) {
   if (n == 0) return;
-  fill_i32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, v, n);
+  launch_k(fill_i32_kernel, (unsigned)((n + 255) / 256), 256, 0, s, p, v, n);
 }
 
 __global__ void advance_kernel(int* positions, const int* tokens, int* out_tokens, int* step, int batch) {
@@ -131,14 +134,14 @@ __global__ void advance_kernel(int* positions, const int* tokens, int* out_token
 
 void launch_advance(int* positions, const int* tokens, int* out_tokens, int* step_counter, int batch,
                     hipStream_t s) {
-  advance_kernel<<<1, 1024, 0, s>>>(positions, tokens, out_tokens, step_counter, batch);
+  launch_k(advance_kernel, 1, 1024, 0, s, positions, tokens, out_tokens, step_counter, batch);
 }
 
 // ---------------------------------------------------------------- argmax
 // Token with the highest logit, lowest index on ties ("Predicción de tokens").
 // Pass 1: each block reduces ARGMAX_CHUNK entries of one row to (value, index);
 // pass 2: one wave per row reduces the block results.
-constexpr int ARGMAX_CHUNK = 4096;
+constexpr int ARGMAX_CHUNK = 1024;  // about 128 blocks per row at a 128K vocabulary
 
 int argmax_blocks(int vocab) { return (vocab + ARGMAX_CHUNK - 1) / ARGMAX_CHUNK; }
 
@@ -193,8 +196,8 @@ void launch_argmax(const float* logits, int rows, int vocab, void* partial, int*
   const int nblk = argmax_blocks(vocab);
   float* pv = (float*)partial;
   int* pi = (int*)(pv + (size_t)rows * nblk);
-  argmax_pass1<<<dim3(nblk, rows), 256, 0, s>>>(logits, vocab, nblk, pv, pi);
-  argmax_pass2<<<rows, 64, 0, s>>>(pv, pi, nblk, out);
+  launch_k(argmax_pass1, dim3(nblk, rows), 256, 0, s, logits, vocab, nblk, pv, pi);
+  launch_k(argmax_pass2, rows, 64, 0, s, pv, pi, nblk, out);
 }
 
 __global__ void __launch_bounds__(1024) argmax_rows_kernel(const float* __restrict__ logits, int vocab,
@@ -218,7 +221,7 @@ __global__ void __launch_bounds__(1024) argmax_rows_kernel(const float* __restri
 
 void launch_argmax_rows(const float* logits, int rows, int vocab, int* out, hipStream_t s) {
   if (rows <= 0) return;
-  argmax_rows_kernel<<<rows, 1024, 0, s>>>(logits, vocab, out);
+  launch_k(argmax_rows_kernel, rows, 1024, 0, s, logits, vocab, out);
 }
 
 }  // namespace llm

@@ -200,16 +200,16 @@ static void gemm_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, c
   const size_t lds = gemm_lds_bytes<BM, BN>();
   switch (ep.kind) {
     case EPI_STORE_F32:
-      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_STORE_F32, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_STORE_F32, NPART, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_RESID:
-      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_RESID, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_RESID, NPART, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_QKV:
-      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_QKV, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_QKV, NPART, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_SWIGLU:
-      gemm_f16_kernel<BM, BN, WGM, WGN, EPI_SWIGLU, NPART, SB><<<grid, nt, lds, s>>>(A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_SWIGLU, NPART, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
   }
 }
@@ -265,15 +265,15 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
   }
 }
 
-// Number of K splits for a GEMM: only small-M shapes whose 64 x 64 tiles cannot fill the
-// GPU (fewer than 384 tiles) are split, aiming at about 512 workgroups, at most 8 splits
-// and at least 4 K steps of 64 per split.
+// Number of K splits for a GEMM: only small-M shapes (weight streaming) whose 64 x 64
+// tiles give fewer than 1024 workgroups are split, aiming at about 1024 workgroups, at
+// most 8 splits and at least 4 K steps of 64 per split.
 int gemm_splitk_count(int M, int N, int K) {
   if (M <= 0 || M > 128 || N % 4 != 0) return 1;
   const long tiles = (long)((M + 63) / 64) * ((N + 63) / 64);
-  if (tiles >= 384) return 1;
+  if (tiles >= 1024) return 1;
   const int nkb = (K + GEMM_BK - 1) / GEMM_BK;
-  int sp = (int)std::min<long>(8, (512 + tiles - 1) / tiles);
+  int sp = (int)std::min<long>(8, (1024 + tiles - 1) / tiles);
   sp = std::min(sp, nkb / 4);
   if (sp < 2) return 1;
   const int per = (nkb + sp - 1) / sp;
@@ -306,10 +306,10 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
     const size_t n4 = (size_t)M * N / 4;
     const dim3 grid((unsigned)((n4 + 255) / 256));
     switch (ep.kind) {
-      case EPI_STORE_F32: splitk_reduce_kernel<EPI_STORE_F32><<<grid, 256, 0, s>>>(splitk_ws, sp, M, N, ep); break;
-      case EPI_RESID: splitk_reduce_kernel<EPI_RESID><<<grid, 256, 0, s>>>(splitk_ws, sp, M, N, ep); break;
-      case EPI_QKV: splitk_reduce_kernel<EPI_QKV><<<grid, 256, 0, s>>>(splitk_ws, sp, M, N, ep); break;
-      case EPI_SWIGLU: splitk_reduce_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(splitk_ws, sp, M, N, ep); break;
+      case EPI_STORE_F32: launch_k(splitk_reduce_kernel<EPI_STORE_F32>, grid, 256, 0, s, splitk_ws, sp, M, N, ep); break;
+      case EPI_RESID: launch_k(splitk_reduce_kernel<EPI_RESID>, grid, 256, 0, s, splitk_ws, sp, M, N, ep); break;
+      case EPI_QKV: launch_k(splitk_reduce_kernel<EPI_QKV>, grid, 256, 0, s, splitk_ws, sp, M, N, ep); break;
+      case EPI_SWIGLU: launch_k(splitk_reduce_kernel<EPI_SWIGLU>, grid, 256, 0, s, splitk_ws, sp, M, N, ep); break;
     }
     return;
   }

@@ -19,6 +19,14 @@
 
 namespace llm {
 
+// fp16 pair (round to nearest even) as a 32-bit word.
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  f16x2_t h;
+  h.x = (f16_t)a;
+  h.y = (f16_t)b;
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 template <typename T, int MR, int R, int EPI, bool NORM>
 __global__ void __launch_bounds__(256) gemv_kernel(const void* __restrict__ Ain, const T* __restrict__ W,
                                                    const float* __restrict__ gnorm, float eps, int M, int N, int K,
@@ -121,7 +129,10 @@ __global__ void __launch_bounds__(256) gemv_kernel(const void* __restrict__ Ain,
 
 // fp16 weights (the bf16-weight path): the same scheme with the weights kept as
 // raw 16-byte words until use, so two chunks x R rows of loads (2R per lane) are
-// issued before any math.
+// issued before any math.  The products use the packed fp16 dot instruction (two
+// products per lane per instruction, fp32 accumulation): fp16 activations are
+// used as loaded, and with the fused norm x * g is rounded to fp16 once, as the
+// separate RMSNorm of the matrix-core path rounds its output.
 
 template <int MR, int R, int EPI, bool NORM>
 __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ain, const f16_t* __restrict__ W,
@@ -134,6 +145,19 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   const int n0 = blockIdx.x * R;
   const int m0 = blockIdx.y * MR;
   const int mrows = min(MR, M - m0);
+
+  // Epilogue inputs that do not depend on the dot products (the residual being
+  // added to, RoPE position / slot / cos / sin) are fetched before the weight
+  // stream so they do not add a dependent round trip after it.
+  const int et = threadIdx.x;
+  const int ei = et / R, er = et % R;
+  const bool ethread = et < MR * R && ei < mrows && n0 + er < N;
+  float e_resid = 0.f;
+  QkvPrep e_qkv = {};
+  if (ethread) {
+    if (EPI == EPI_RESID) e_resid = ep.out_f32[(size_t)(m0 + ei) * ep.ld + n0 + er];
+    if (EPI == EPI_QKV) e_qkv = qkv_prepare(ep, m0 + ei, n0 + er);
+  }
 
   const f16_t* wr[R];
 #pragma unroll
@@ -170,23 +194,29 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
         if (i < mrows) {
-          float a[8];
+          // the 8 activations of this lane as 4 fp16 pairs
+          uint32_t ah[4];
           if (NORM) {
+            float a[8];
             load8(reinterpret_cast<const float*>(Ain) + (size_t)(m0 + i) * K + kk[u], a);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              ss[i] = fmaf(a[e], a[e], ss[i]);
-              a[e] *= g[e];
-            }
+            for (int e = 0; e < 8; ++e) ss[i] = fmaf(a[e], a[e], ss[i]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ah[e] = pack_h2(a[2 * e] * g[2 * e], a[2 * e + 1] * g[2 * e + 1]);
           } else {
-            load8(reinterpret_cast<const f16_t*>(Ain) + (size_t)(m0 + i) * K + kk[u], a);
+            const u32x4_t raw =
+                *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const f16_t*>(Ain) + (size_t)(m0 + i) * K + kk[u]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ah[e] = raw[e];
           }
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            float w[8];
-            f16x8_to_f32(wraw[u][r], w);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[i][r] = fmaf(a[e], w[e], acc[i][r]);
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t wv = wraw[u][r][e];
+              acc[i][r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, ah[e]), __builtin_bit_cast(f16x2_t, wv),
+                                                 acc[i][r], false);
+            }
           }
         }
       }
@@ -209,28 +239,25 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   }
   __syncthreads();
 
-  const int t = threadIdx.x;
-  if (t < MR * R) {
-    const int i = t / R, r = t % R;
+  if (ethread) {
+    const int i = ei, r = er;
     const int m = m0 + i, n = n0 + r;
-    if (i < mrows && n < N) {
-      float v = s_acc[0][i][r] + s_acc[1][i][r] + s_acc[2][i][r] + s_acc[3][i][r];
-      float vp = s_acc[0][i][r ^ 1] + s_acc[1][i][r ^ 1] + s_acc[2][i][r ^ 1] + s_acc[3][i][r ^ 1];
-      if (NORM) {
-        const float tot = s_ss[0][i] + s_ss[1][i] + s_ss[2][i] + s_ss[3][i];
-        const float inv = 1.0f / sqrtf(tot / (float)K + eps);
-        v *= inv;
-        vp *= inv;
-      }
-      if (EPI == EPI_STORE_F32) {
-        ep.out_f32[(size_t)m * ep.ld + n] = v;
-      } else if (EPI == EPI_RESID) {
-        ep.out_f32[(size_t)m * ep.ld + n] += v;
-      } else if (EPI == EPI_QKV) {
-        epi_qkv<f16_t>(ep, m, n, v, vp);
-      } else if (EPI == EPI_SWIGLU) {
-        if ((r & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
-      }
+    float v = s_acc[0][i][r] + s_acc[1][i][r] + s_acc[2][i][r] + s_acc[3][i][r];
+    float vp = s_acc[0][i][r ^ 1] + s_acc[1][i][r ^ 1] + s_acc[2][i][r ^ 1] + s_acc[3][i][r ^ 1];
+    if (NORM) {
+      const float tot = s_ss[0][i] + s_ss[1][i] + s_ss[2][i] + s_ss[3][i];
+      const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+      v *= inv;
+      vp *= inv;
+    }
+    if (EPI == EPI_STORE_F32) {
+      ep.out_f32[(size_t)m * ep.ld + n] = v;
+    } else if (EPI == EPI_RESID) {
+      ep.out_f32[(size_t)m * ep.ld + n] = e_resid + v;
+    } else if (EPI == EPI_QKV) {
+      qkv_store<f16_t>(ep, e_qkv, m, n, v, vp);
+    } else if (EPI == EPI_SWIGLU) {
+      if ((r & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
     }
   }
 }
@@ -241,11 +268,11 @@ static void gemv_h_dispatch(const void* A, const f16_t* W, const float* g, float
   dim3 grid((N + R - 1) / R, (M + MR - 1) / MR);
   switch (ep.kind) {
     case EPI_STORE_F32:
-      gemv_h_kernel<MR, R, EPI_STORE_F32, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep);
+      launch_k(gemv_h_kernel<MR, R, EPI_STORE_F32, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep);
       break;
-    case EPI_RESID: gemv_h_kernel<MR, R, EPI_RESID, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
-    case EPI_QKV: gemv_h_kernel<MR, R, EPI_QKV, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
-    case EPI_SWIGLU: gemv_h_kernel<MR, R, EPI_SWIGLU, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+    case EPI_RESID: launch_k(gemv_h_kernel<MR, R, EPI_RESID, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep); break;
+    case EPI_QKV: launch_k(gemv_h_kernel<MR, R, EPI_QKV, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep); break;
+    case EPI_SWIGLU: launch_k(gemv_h_kernel<MR, R, EPI_SWIGLU, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep); break;
   }
 }
 
@@ -255,11 +282,11 @@ static void gemv_dispatch(const void* A, const T* W, const float* g, float eps, 
   dim3 grid((N + R - 1) / R, (M + MR - 1) / MR);
   switch (ep.kind) {
     case EPI_STORE_F32:
-      gemv_kernel<T, MR, R, EPI_STORE_F32, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep);
+      launch_k(gemv_kernel<T, MR, R, EPI_STORE_F32, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep);
       break;
-    case EPI_RESID: gemv_kernel<T, MR, R, EPI_RESID, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
-    case EPI_QKV: gemv_kernel<T, MR, R, EPI_QKV, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
-    case EPI_SWIGLU: gemv_kernel<T, MR, R, EPI_SWIGLU, NORM><<<grid, 256, 0, s>>>(A, W, g, eps, M, N, K, ep); break;
+    case EPI_RESID: launch_k(gemv_kernel<T, MR, R, EPI_RESID, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep); break;
+    case EPI_QKV: launch_k(gemv_kernel<T, MR, R, EPI_QKV, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep); break;
+    case EPI_SWIGLU: launch_k(gemv_kernel<T, MR, R, EPI_SWIGLU, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep); break;
   }
 }
 

@@ -1,10 +1,32 @@
 // Internal launchers of the decoder-pass kernels (host side of each .hip file).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace llm {
+
+// Kernel timing hook.  While a timer is installed on the calling thread (kernel
+// timing switched on for a model), every launch takes a start / stop event pair
+// from it and records them with the dispatch itself (hipExtLaunchKernelGGL), so
+// the measured span is the kernel's own execution, not the queue around it.
+struct LaunchTimer {
+  virtual bool take(hipEvent_t* start, hipEvent_t* stop) = 0;
+  virtual void done(hipEvent_t start, hipEvent_t stop) = 0;
+};
+extern thread_local LaunchTimer* g_launch_timer;
+
+template <typename F, typename... Args>
+inline void launch_k(F kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args... args) {
+  hipEvent_t a, b;
+  if (g_launch_timer && g_launch_timer->take(&a, &b)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, s, a, b, 0u, args...);
+    g_launch_timer->done(a, b);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, s, args...);
+  }
+}
 
 // What a projection does with its fp32 result C[m][n] = sum_k A[m][k] * W[n][k].
 enum EpiKind : int {

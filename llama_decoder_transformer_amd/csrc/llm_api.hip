@@ -169,6 +169,10 @@ struct llm_model {
   double t_ms[LLM_K_COUNT] = {};
 };
 
+namespace llm {
+thread_local LaunchTimer* g_launch_timer = nullptr;
+}
+
 namespace {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -184,21 +188,40 @@ hipEvent_t take_event(llm_model* m) {
   return e;
 }
 
-// Brackets the launches made during its lifetime with two events when timing is on.
+// While alive (and kernel timing is on), installs a launch timer on this thread:
+// each kernel launched in its scope records a start / stop event pair with its
+// dispatch, charged to group `kind`.  One Timed scope counts as one invocation.
+struct ModelTimer final : LaunchTimer {
+  llm_model* m = nullptr;
+  int kind = 0;
+  bool take(hipEvent_t* a, hipEvent_t* b) override {
+    *a = take_event(m);
+    if (!*a) return false;
+    *b = take_event(m);
+    if (!*b) {
+      m->event_pool.push_back(*a);
+      return false;
+    }
+    return true;
+  }
+  void done(hipEvent_t a, hipEvent_t b) override { m->pending.push_back({kind, a, b}); }
+};
+
 struct Timed {
-  llm_model* m;
-  int kind;
-  hipStream_t s;
-  hipEvent_t a = nullptr;
-  Timed(llm_model* m_, int kind_, hipStream_t s_) : m(m_), kind(kind_), s(s_) {
-    if (m->timing && (a = take_event(m))) (void)hipEventRecord(a, s);
+  ModelTimer timer;
+  LaunchTimer* prev = nullptr;
+  bool on = false;
+  Timed(llm_model* m, int kind, hipStream_t) {
+    if (!m->timing) return;
+    timer.m = m;
+    timer.kind = kind;
+    prev = g_launch_timer;
+    g_launch_timer = &timer;
+    m->t_launches[kind] += 1;
+    on = true;
   }
   ~Timed() {
-    if (!a) return;
-    hipEvent_t b = take_event(m);
-    if (!b) return;
-    (void)hipEventRecord(b, s);
-    m->pending.push_back({kind, a, b});
+    if (on) g_launch_timer = prev;
   }
 };
 
@@ -211,7 +234,6 @@ llm_status resolve_timing(llm_model* m) {
       m->pending.clear();
       return LLM_ERR_HIP;
     }
-    m->t_launches[br.kind] += 1;
     m->t_ms[br.kind] += ms;
     m->event_pool.push_back(br.a);
     m->event_pool.push_back(br.b);
