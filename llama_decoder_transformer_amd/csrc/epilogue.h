@@ -74,11 +74,107 @@ __device__ __forceinline__ void epi_qkv(const EpiParams& p, int m, int n, float 
   qkv_store<TA>(p, qkv_prepare(p, m, n), m, n, v, vp);
 }
 
+// q|k|v epilogue of an MFMA tile held as acc[FM][FN] (16 x 16 blocks; this lane holds rows
+// m_base + 16 i + 4 lg + r of column n_base + 16 jn + l16).  The column's role (q, k or v),
+// head, RoPE pair, destination base and row stride depend only on the column, so they are
+// decoded once per block column; the rotation is written without branches (sign of the
+// partner term from the column parity; cos 1 and sin 0 for v columns).  All lanes must
+// call it (the RoPE partner comes from lane ^ 1).
+//
+// STAGED: the rows are a prefill run (positions pos0 + m, slot slot0, ranges checked by the
+// caller) and the tile's rows of the RoPE table are staged in s_cos / s_sin (row m at
+// (m - m_tile) * d/2).  Otherwise each element validates its row (decode rows carry their
+// own position and slot) and reads the global table.
+template <int FM, int FN, bool STAGED>
+__device__ __forceinline__ void qkv_tile_epilogue(const EpiParams& p, const f32x4_t (&acc)[FM][FN], int M, int N,
+                                                  int m_base, int n_base, int lg, int l16,
+                                                  const float* s_cos = nullptr, const float* s_sin = nullptr,
+                                                  int m_tile = 0) {
+  const int d = p.head_dim, half = d >> 1;
+  const int qd = p.n_heads * d, kd = p.n_kv_heads * d;
+#pragma unroll
+  for (int jn = 0; jn < FN; ++jn) {
+    const int n = n_base + jn * 16 + l16;
+    const int kind = n < qd ? 0 : (n < qd + kd ? 1 : 2);
+    const int col = kind == 0 ? n : (kind == 1 ? n - qd : n - qd - kd);
+    const int g = col / d, e = col - g * d;
+    const int j = e >> 1;
+    const bool rot = kind < 2;
+    const float sgn = (n & 1) ? 1.f : -1.f;
+    f16_t* const cache = reinterpret_cast<f16_t*>(kind == 1 ? p.k_cache : p.v_cache);
+    if constexpr (STAGED) {
+      f16_t* const dst = kind == 0
+          ? reinterpret_cast<f16_t*>(p.out_act) + n
+          : cache + (((size_t)p.slot0 * p.n_kv_heads + g) * p.max_seq + p.pos0) * d + e;
+      const size_t rstride = kind == 0 ? (size_t)p.ld : (size_t)d;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = acc[i][jn][r];
+          const float vp = lane_xor1(v);
+          const int m = m_base + i * 16 + lg * 4 + r;
+          if (m < M && n < N) {
+            const int t = (m - m_tile) * half + j;
+            const float c = rot ? s_cos[t] : 1.f;
+            const float sn = rot ? s_sin[t] : 0.f;
+            dst[(size_t)m * rstride] = (f16_t)fmaf(sgn * vp, sn, v * c);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = acc[i][jn][r];
+          const float vp = lane_xor1(v);
+          const int m = m_base + i * 16 + lg * 4 + r;
+          int pos, slot;
+          if (m < M && n < N && epi_row(p, m, pos, slot)) {
+            const float c = rot ? p.rope_cos[(size_t)pos * half + j] : 1.f;
+            const float sn = rot ? p.rope_sin[(size_t)pos * half + j] : 0.f;
+            const f16_t out = (f16_t)fmaf(sgn * vp, sn, v * c);
+            if (kind == 0) reinterpret_cast<f16_t*>(p.out_act)[(size_t)m * p.ld + n] = out;
+            else cache[(((size_t)slot * p.n_kv_heads + g) * p.max_seq + pos) * d + e] = out;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Residual add of an MFMA tile (layout as in qkv_tile_epilogue): all residual values are
+// loaded first, then all sums stored, so the loads are in flight together instead of
+// each waiting behind the previous element's store.
+template <int FM, int FN>
+__device__ __forceinline__ void resid_tile_epilogue(float* out, int ld, f32x4_t (&acc)[FM][FN], int M, int N,
+                                                    int m_base, int n_base, int lg, int l16) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m_base + i * 16 + lg * 4 + r, n = n_base + jn * 16 + l16;
+        if (m < M && n < N) acc[i][jn][r] += out[(size_t)m * ld + n];
+      }
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m_base + i * 16 + lg * 4 + r, n = n_base + jn * 16 + l16;
+        if (m < M && n < N) out[(size_t)m * ld + n] = acc[i][jn][r];
+      }
+}
+
 // SwiGLU of one output column c from its gate (w1) and up (w3) values.
 template <typename TA>
 __device__ __forceinline__ void epi_swiglu(const EpiParams& p, int m, int c, float gate, float up) {
   const float LOG2E = 1.4426950408889634f;
-  const float sg = gate / (1.0f + exp2f(-gate * LOG2E));
+  const float sg = gate * __builtin_amdgcn_rcpf(1.0f + exp2f(-gate * LOG2E));
   reinterpret_cast<TA*>(p.out_act)[(size_t)m * p.ld + c] = from_f32<TA>(sg * up);
 }
 

@@ -159,7 +159,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
   }
 
   // Epilogue.  A split-K workgroup stores its partial sums to slice blockIdx.y.
+  if constexpr (EPI == EPI_QKV) {
+    qkv_tile_epilogue<FM, FN, false>(ep, acc, M, N, tm + wm * WM, tn + wn * WN, lg, l16);
+    return;
+  }
   float* const out_f32 = ep.out_f32 + (size_t)blockIdx.y * M * ep.ld;
+  if constexpr (EPI == EPI_RESID) {
+    resid_tile_epilogue<FM, FN>(out_f32, ep.ld, acc, M, N, tm + wm * WM, tn + wn * WN, lg, l16);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -169,12 +177,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
         const int m = tm + wm * WM + i * 16 + lg * 4 + r;
         const int n = tn + wn * WN + jn * 16 + l16;
         const float v = acc[i][jn][r];
-        if (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
-          const float vp = __shfl_xor(v, 1);
-          if (m < M && n < N) {
-            if (EPI == EPI_QKV) epi_qkv<f16_t>(ep, m, n, v, vp);
-            else if ((n & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
-          }
+        if (EPI == EPI_SWIGLU) {
+          const float vp = lane_xor1(v);
+          if (m < M && n < N && (n & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
         } else if (m < M && n < N) {
           if (EPI == EPI_STORE_F32) out_f32[(size_t)m * ep.ld + n] = v;
           else out_f32[(size_t)m * ep.ld + n] += v;
@@ -184,14 +189,288 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
   }
 }
 
+// ------------------------------------------------------------------ LDS-DMA variant
+//
+// Same tiling and epilogue, but the global loads go straight into LDS
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the instruction's LDS
+// base + 16 * lane), so no registers stage the tiles and NS stages rotate through
+// LDS: one holds the k-step being multiplied (its fragments already in registers),
+// one the k-step whose fragments are being read, and NS - 2 are in flight, so a
+// stage's loads have NS - 2 k-steps to land.  BK = 32 per stage
+// (one MFMA k-step): a tile row is 64 bytes = 4 chunks of 16 bytes, stored at
+// chunk c ^ ((r / 2) % 4) so that the 8 lanes of one LDS read cycle (8
+// consecutive rows, one chunk) hit distinct banks.  One DMA instruction fills 16
+// rows; lane l takes row l / 4 and physical chunk l % 4, i.e. the logical chunk
+// (l % 4) ^ ((l / 8) % 4) of that row.  Rows past M or N load a clamped row (their
+// results are discarded); K must be a multiple of 32.
+
+constexpr int DS_BK = 32;
+
+// Tile of workgroup `id` for the DMA kernel.  Workgroups are dealt to the 8 XCDs
+// round-robin (XCD = id % 8, j = id / 8 is the order within one XCD).  When the N
+// tiles split evenly, XCD x owns the band of N tiles [x * tn / 8, (x + 1) * tn / 8),
+// walked in groups of GM M tiles: the about 32 workgroups an XCD runs at once then
+// cover GM M tiles x a few N tiles, so each A and W k-slice they read is shared in
+// that XCD's L2 by several tiles (a column-major walk shares W only, and streams
+// all of A once per N tile).  Otherwise: contiguous N-major runs per XCD.
+__device__ __forceinline__ void dma_tile_of(int id, int tiles_m, int tiles_n, int& tm_idx, int& tn_idx) {
+  constexpr int GM = 8;
+  const int xcd = id % 8, j = id / 8;
+  if (tiles_n % 8 == 0) {
+    const int band = tiles_n / 8;
+    const int full = tiles_m / GM, rem = tiles_m % GM;
+    const int g = j / (GM * band);
+    if (g < full) {
+      const int r = j % (GM * band);
+      tm_idx = g * GM + r % GM;
+      tn_idx = xcd * band + r / GM;
+    } else {
+      const int r = j - full * GM * band;
+      tm_idx = full * GM + r % rem;
+      tn_idx = xcd * band + r / rem;
+    }
+    return;
+  }
+  const int T = tiles_m * tiles_n;
+  const int per = T / 8, rm = T % 8;
+  const int t = (xcd < rm ? xcd * (per + 1) : rm * (per + 1) + (xcd - rm) * per) + j;
+  tn_idx = t / tiles_m;
+  tm_idx = t % tiles_m;
+}
+
+__device__ __forceinline__ int ds_off(int r, int c) { return r * DS_BK + ((c ^ ((r >> 1) & 3)) << 3); }
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
+template <int V>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(V >= 0 && V < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int EPI, bool PIPE>
+__global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* __restrict__ A,
+                                                                  const f16_t* __restrict__ W, int M, int N, int K,
+                                                                  int tiles_m, int tiles_n, EpiParams ep) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int STAGE = (BM + BN) * DS_BK;  // f16 elements per stage
+  constexpr int NI = (BM + BN) / 16;        // DMA instructions per stage
+  constexpr int PW = NI / NW;               // ... per wave
+  static_assert(NI % NW == 0, "DMA instructions do not split evenly over the waves");
+  static_assert(NS >= 3 && NS <= 5, "stages");
+
+  extern __shared__ __attribute__((aligned(16))) f16_t smem[];
+
+  int tm_idx, tn_idx;
+  dma_tile_of(blockIdx.x, tiles_m, tiles_n, tm_idx, tn_idx);
+  const int tm = tm_idx * BM, tn = tn_idx * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WGN, wn = wid % WGN;
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  // This lane's source row offsets (elements) and logical chunk for each of the wave's DMA instructions.
+  const int dr = lane >> 2;
+  const int dc = ((lane & 3) ^ ((dr >> 1) & 3)) * 8;
+  const f16_t* src[PW];
+  int dst_off[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int blk = wid + NW * i;  // 16-row block of the stage: A blocks first, then W blocks
+    if (blk < BM / 16) {
+      src[i] = A + (size_t)min(tm + blk * 16 + dr, M - 1) * K + dc;
+      dst_off[i] = blk * 16 * DS_BK;
+    } else {
+      const int b = blk - BM / 16;
+      src[i] = W + (size_t)min(tn + b * 16 + dr, N - 1) * K + dc;
+      dst_off[i] = BM * DS_BK + b * 16 * DS_BK;
+    }
+  }
+  auto issue = [&](int stage_buf, int k0) {
+    f16_t* base = smem + stage_buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src[i] + k0),
+                                       (void __attribute__((address_space(3)))*)(base + dst_off[i]), 16, 0, 0);
+  };
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Fragments are double-buffered in registers: the reads of k-step kt+1 are issued
+  // before the MFMAs of k-step kt, so the matrix cores do not wait on LDS latency.
+  f16x8_t af[2][FM], bw[2][FN];
+  auto read_frags = [&](f16x8_t* a, f16x8_t* b, int stage_buf) {
+    const f16_t* As = smem + stage_buf * STAGE;
+    const f16_t* Bs = As + BM * DS_BK;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const f16x8_t*>(&As[ds_off(wm * WM + i * 16 + l16, lg)]);
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) b[jn] = *reinterpret_cast<const f16x8_t*>(&Bs[ds_off(wn * WN + jn * 16 + l16, lg)]);
+  };
+  auto mfmas = [&](const f16x8_t* a, const f16x8_t* b) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < FN; ++jn)
+        acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[jn], acc[i][jn], 0, 0, 0);
+  };
+  // Stage st's loads are complete once at most min(depth, nk - 1 - st) later stages are
+  // outstanding, depth being the number of stages issued after st so far; after every wave has
+  // waited for its own part and passed the barrier, the stage is in LDS.
+  auto stage_ready = [&](int st, int nk, int depth) {
+    const int later = min(depth, nk - 1 - st);
+    if (later >= 3) wait_vmcnt<3 * PW>();
+    else if (later == 2) wait_vmcnt<2 * PW>();
+    else if (later == 1) wait_vmcnt<PW>();
+    else wait_vmcnt<0>();
+    // A bare barrier: __syncthreads() would add a release fence that waits for all loads in flight.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  const int nk = K / DS_BK;
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st, st * DS_BK);
+  if constexpr (!PIPE) {
+    // Iteration kt: make stage kt visible (NS-2 later stages may still be in flight), refill the
+    // buffer of stage kt-1 (every wave finished reading it before this barrier), read and multiply.
+    for (int kt = 0; kt < nk; ++kt) {
+      stage_ready(kt, nk, NS - 2);
+      if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, (kt + NS - 1) * DS_BK);
+      read_frags(af[0], bw[0], kt % NS);
+      mfmas(af[0], bw[0]);
+    }
+  } else {
+    stage_ready(0, nk, NS - 2);  // stages 1 .. NS-2 issued after stage 0
+    read_frags(af[0], bw[0], 0);
+
+    // Iteration kt: make stage kt+1 visible (stages up to kt+NS-2 have been issued, so NS-3 may
+    // still be in flight behind it), refill the buffer of stage kt-1 (every wave read its fragments
+    // before the MFMAs of iteration kt-1, which precede this barrier), read stage kt+1's
+    // fragments, then run stage kt's MFMAs.  Unrolled by two so the fragment buffers have fixed
+    // registers.
+    auto iter = [&](int kt, f16x8_t* a_cur, f16x8_t* b_cur, f16x8_t* a_nxt, f16x8_t* b_nxt) {
+      if (kt + 1 < nk) {
+        stage_ready(kt + 1, nk, NS - 3);
+        if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, (kt + NS - 1) * DS_BK);
+        read_frags(a_nxt, b_nxt, (kt + 1) % NS);
+      }
+      mfmas(a_cur, b_cur);
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      iter(kt, af[0], bw[0], af[1], bw[1]);
+      if (kt + 1 < nk) iter(kt + 1, af[1], bw[1], af[0], bw[0]);
+    }
+  }
+
+  if constexpr (EPI == EPI_QKV) {
+    // Prefill rows only (positions pos0 + m, slot slot0, ranges checked by the host, and the
+    // table rows fit the stage buffers; the launcher sends other q|k|v projections to the
+    // register-staged kernel).  The tile stages its rows of the RoPE table (cos and sin, d/2
+    // each) in the idle LDS stage buffers with coalesced loads, so the epilogue reads hit LDS.
+    const int half = ep.head_dim >> 1;
+    __syncthreads();  // every wave is done with the stage buffers
+    float* s_cos = reinterpret_cast<float*>(smem);
+    float* s_sin = s_cos + BM * half;
+    const int rows = min(BM, M - tm);
+    for (int idx = tid; idx < rows * half; idx += NW * 64) {
+      const size_t src = (size_t)(ep.pos0 + tm) * half + idx;  // rows are consecutive positions
+      s_cos[idx] = ep.rope_cos[src];
+      s_sin[idx] = ep.rope_sin[src];
+    }
+    __syncthreads();
+    qkv_tile_epilogue<FM, FN, true>(ep, acc, M, N, tm + wm * WM, tn + wn * WN, lg, l16, s_cos, s_sin, tm);
+    return;
+  }
+  if constexpr (EPI == EPI_RESID) {
+    resid_tile_epilogue<FM, FN>(ep.out_f32, ep.ld, acc, M, N, tm + wm * WM, tn + wn * WN, lg, l16);
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = tm + wm * WM + i * 16 + lg * 4 + r;
+        const int n = tn + wn * WN + jn * 16 + l16;
+        const float v = acc[i][jn][r];
+        if (EPI == EPI_SWIGLU) {
+          const float vp = lane_xor1(v);
+          if (m < M && n < N && (n & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
+        } else if (m < M && n < N) {
+          if (EPI == EPI_STORE_F32) ep.out_f32[(size_t)m * ep.ld + n] = v;
+          else ep.out_f32[(size_t)m * ep.ld + n] += v;
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int NPART = 1, bool SB = false>
+static void gemm_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep, hipStream_t s,
+                          int splits = 1);
+
+template <int BM, int BN, int NS>
+static constexpr size_t gemm_dma_lds_bytes() {
+  return (size_t)NS * (BM + BN) * DS_BK * sizeof(f16_t);
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, bool PIPE = false>
+static void gemm_dma_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep,
+                              hipStream_t s) {
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const dim3 grid(tm * tn);
+  const int nt = 64 * WGM * WGN;
+  constexpr size_t lds = gemm_dma_lds_bytes<BM, BN, NS>();
+  static bool attr = false;  // above 64 KiB the per-kernel dynamic LDS limit must be raised once
+  if (!attr) {
+    attr = true;
+    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_STORE_F32, PIPE>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_RESID, PIPE>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_QKV, PIPE>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_SWIGLU, PIPE>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  }
+  switch (ep.kind) {
+    case EPI_STORE_F32:
+      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_STORE_F32, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep);
+      break;
+    case EPI_RESID:
+      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_RESID, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep);
+      break;
+    case EPI_QKV:
+      // The staged RoPE rows (BM x d floats, d <= 128) fit only square 4-stage tiles; other
+      // tiles hand the q|k|v projection to the register-staged kernel.
+      if constexpr (BM == BN && NS >= 4)
+        launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_QKV, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep);
+      else
+        gemm_dispatch<128, 128, 2, 2>(A, W, M, N, K, ep, s);
+      break;
+    case EPI_SWIGLU:
+      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_SWIGLU, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep);
+      break;
+  }
+}
+
 template <int BM, int BN>
 static size_t gemm_lds_bytes() {
   return (size_t)2 * (BM + BN) * GEMM_LDK * sizeof(f16_t);
 }
 
-template <int BM, int BN, int WGM, int WGN, int NPART = 1, bool SB = false>
+template <int BM, int BN, int WGM, int WGN, int NPART, bool SB>
 static void gemm_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep, hipStream_t s,
-                          int splits = 1) {
+                          int splits) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int nkb = (K + GEMM_BK - 1) / GEMM_BK;
   const int kb_per = (nkb + splits - 1) / splits;
@@ -285,10 +564,11 @@ size_t gemm_splitk_floats(int M, int N, int K) {
   return sp > 1 ? (size_t)sp * M * N : 0;
 }
 
-// Tile choice from a sweep of the Llama-3-8B projection shapes at M = 512, 2048
-// and 8192 on MI355X: the 8-wave 256 x 256 tile when it still yields at least 192
-// tiles, then 128 x 128 with at least 256 tiles (one per CU), else 64 x 64, split
-// over K when even those are too few.
+// Tile choice from a sweep of the Llama-3-8B projection shapes at M = 512, 2048 and
+// 8192 on MI355X.  Shapes with K % 32 == 0 use the LDS-DMA kernel: the 8-wave 256 x 256
+// tile when it still yields at least 192 tiles, 256 x 128 with at least 256, 128 x 128
+// with at least 192, else 64 x 64.  Other K use the register-staged kernel.  Small M
+// whose tiles cannot fill the GPU is split over K first.
 void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep, float* splitk_ws,
                      size_t splitk_ws_floats, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
@@ -313,8 +593,23 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
     }
     return;
   }
-  // The q|k|v epilogue (RoPE table reads, cache addressing) does not fit the 256 x 256
-  // tile's registers (it spills), so that projection stays on 128 x 128 tiles.
+  // The DMA kernel's q|k|v epilogue handles prefill rows whose RoPE table rows (BM x d floats)
+  // fit its stage buffers: BM = BN square tiles with 4 stages hold d <= 128.
+  const bool qkv = ep.kind == EPI_QKV;
+  const bool dma_qkv_ok = ep.row_pos == nullptr && ep.head_dim <= 128;
+  if (K % DS_BK == 0 && (!qkv || dma_qkv_ok)) {
+    if (tiles(256, 256) >= 192)
+      gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
+    else if (!qkv && tiles(256, 128) >= 256)
+      gemm_dma_dispatch<256, 128, 4, 2, 4>(a, w, M, N, K, ep, s);
+    else if (tiles(128, 128) >= 192)
+      gemm_dma_dispatch<128, 128, 2, 2, 4>(a, w, M, N, K, ep, s);
+    else
+      gemm_dma_dispatch<64, 64, 2, 2, 4>(a, w, M, N, K, ep, s);
+    return;
+  }
+  // The q|k|v epilogue (RoPE table reads, cache addressing) does not fit the register-staged
+  // 256 x 256 tile's registers (it spills), so that projection stays on 128 x 128 tiles.
   if (M > 128 && ep.kind != EPI_QKV && tiles(256, 256) >= 192)
     gemm_dispatch<256, 256, 2, 4, 1, true>(a, w, M, N, K, ep, s);
   else if (M > 64 && tiles(128, 128) >= 256)
