@@ -245,3 +245,94 @@ def test_prefill_is_deterministic_and_causal():
     m.prefill(_i32(p2))
     d = m.prefill(_i32(p2[:100])).cpu().numpy()
     assert np.array_equal(c, d)
+
+
+# ---------------------------------------------------------------- prefill from a non-empty cache
+
+def test_chunked_prefill_bf16_matches_oracle():
+    """A prompt prefilled in three chunks (start_pos 0, 100, 177), then one decode step, equals the
+    oracle's single prefill and decode (the KV cache makes the two orders the same computation)."""
+    shape = SMALL_BF16
+    hw = host_weights(shape, seed=6)
+    S = 300
+    prompt = inputs.token_ids(shape.vocab_size, S, sub=6)
+    om = OracleModel(oracle_config(shape), oracle_weights(hw, np.float64))
+    ref_logits, cache = om.prefill(prompt)
+    nxt = int(np.argmax(ref_logits))
+    ref_dec = om.decode(nxt, S, cache)
+    m = _model(shape, hw, max_batch=1, max_prefill=S)
+    for a, b in ((0, 100), (100, 177), (177, S)):
+        lg = m.prefill(_i32(prompt[a:b]), start_pos=a).cpu().numpy()
+    e_pre = rel_err(lg, ref_logits)
+    whole = m.prefill(_i32(prompt)).cpu().numpy()
+    e_whole = rel_err(lg, whole)
+    m.prefill(_i32(prompt[:177]))
+    m.prefill(_i32(prompt[177:]), start_pos=177)
+    dec = m.decode_step(_i32([0]), _i32([S]), _i32([nxt])).cpu().numpy()[0]
+    e_dec = rel_err(dec, ref_dec)
+    print(f"[chunked prefill bf16] rel err {e_pre:.3e} (vs one-shot GPU {e_whole:.3e}), decode {e_dec:.3e}", flush=True)
+    assert e_pre <= TOL_BF16 and e_dec <= TOL_BF16 and e_whole <= TOL_BF16
+    assert near_tie_ok(int(np.argmax(lg)), ref_logits, TOL_BF16)
+    assert m.read_device_error() == 0
+
+
+def test_chunked_prefill_fp32_matches_oracle(stories):
+    shape, hw, prompt, toks, ref_logits = stories
+    m = _model(shape, hw, max_batch=1, max_prefill=len(prompt))
+    m.prefill(_i32(prompt[:3]))
+    lg = m.prefill(_i32(prompt[3:]), start_pos=3).cpu().numpy()
+    e = rel_err(lg, ref_logits[0])
+    print(f"[chunked prefill fp32] rel err {e:.3e}", flush=True)
+    assert e <= TOL_F32
+    assert int(np.argmax(lg)) == int(toks[0])
+
+
+# ---------------------------------------------------------------- other head groupings: MQA and MHA
+
+HEAD_SHAPES = {
+    # multi-query: one KV head for 8 query heads (MFMA prefill with 4-head packing, MFMA decode)
+    "mqa-8x1": SMALL_BF16.replace(name="mqa-8x1", dim=1024, n_heads=8, n_kv_heads=1, n_layers=2),
+    # multi-query, 32 query heads per KV head (decode takes the vector kernel: more heads than MFMA columns)
+    "mqa-32x1": SMALL_BF16.replace(name="mqa-32x1", dim=4096, n_heads=32, n_kv_heads=1, n_layers=1),
+    # multi-head: as many KV heads as query heads
+    "mha-4x4": SMALL_BF16.replace(name="mha-4x4", dim=512, n_heads=4, n_kv_heads=4, n_layers=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(HEAD_SHAPES))
+def test_head_groupings_prefill_and_decode_match_oracle(name):
+    shape = HEAD_SHAPES[name]
+    hw = host_weights(shape, seed=8)
+    S = 150
+    prompt = inputs.token_ids(shape.vocab_size, S, sub=8)
+    om = OracleModel(oracle_config(shape), oracle_weights(hw, np.float64))
+    ref_toks, ref_logits = om.generate(prompt, 2)
+    m = _model(shape, hw, max_batch=1, max_prefill=S)
+    lg = m.prefill(_i32(prompt)).cpu().numpy()
+    errs = [rel_err(lg, ref_logits[0])]
+    for s in range(2):
+        lg = m.decode_step(_i32([0]), _i32([S + s]), _i32([ref_toks[s]])).cpu().numpy()[0]
+        errs.append(rel_err(lg, ref_logits[s + 1]))
+    print(f"[{name}] rel errs {np.round(errs, 6).tolist()}", flush=True)
+    assert max(errs) <= TOL_BF16
+    assert m.read_device_error() == 0
+
+
+def test_llama2_7b_shaped_mha_layer_matches_oracle():
+    """One Llama-2-7B-shaped layer (dim 4096, 32 query and 32 KV heads, FFN 11008), S = 512."""
+    shape = inputs.ModelShape("llama2-7b-layer", dim=4096, n_layers=1, n_heads=32, n_kv_heads=32,
+                              ffn_hidden_dim=11008, vocab_size=256, max_seq_len=4096, rope_theta=10000.0,
+                              norm_eps=1e-5, dtype="bf16")
+    hw = host_weights(shape, seed=9)
+    S = 512
+    m = _model(shape, hw, max_batch=1, max_prefill=S)
+    x = inputs.bf16_bits_to_f32(inputs.activations_bf16_bits(S, shape.dim, seed=9))
+    xd = torch.from_numpy(x.copy()).to(DEV)
+    m.layer_forward(0, xd)
+    got = xd.cpu().numpy()
+    del m
+    om = OracleModel(oracle_config(shape), oracle_weights(hw, np.float32))
+    ref = om.layer(0, x.astype(np.float64), om.new_cache(S), np.arange(S))
+    e = rel_err(got - x, ref - x)
+    print(f"[llama2-7b MHA layer S={S}] delta rel err {e:.3e}", flush=True)
+    assert e <= TOL_BF16
