@@ -250,7 +250,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int BM, int BN, int WGM, int WGN, int NS, int EPI, bool PIPE>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* __restrict__ A,
                                                                   const f16_t* __restrict__ W, int M, int N, int K,
-                                                                  int tiles_m, int tiles_n, EpiParams ep) {
+                                                                  int tiles_m, int tiles_n, EpiParams ep,
+                                                                  int kb_per) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 16, FN = WN / 16;
@@ -270,6 +271,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
   const int wm = wid / WGN, wn = wid % WGN;
   const int l16 = lane & 15, lg = lane >> 4;
 
+  // K range of this workgroup: kb_per k-steps starting at split blockIdx.y (all of K unsplit).
+  const int kb0 = blockIdx.y * kb_per;
+  const int kbase = kb0 * DS_BK;
+
   // This lane's source row offsets (elements) and logical chunk for each of the wave's DMA instructions.
   const int dr = lane >> 2;
   const int dc = ((lane & 3) ^ ((dr >> 1) & 3)) * 8;
@@ -279,11 +284,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
   for (int i = 0; i < PW; ++i) {
     const int blk = wid + NW * i;  // 16-row block of the stage: A blocks first, then W blocks
     if (blk < BM / 16) {
-      src[i] = A + (size_t)min(tm + blk * 16 + dr, M - 1) * K + dc;
+      src[i] = A + (size_t)min(tm + blk * 16 + dr, M - 1) * K + kbase + dc;
       dst_off[i] = blk * 16 * DS_BK;
     } else {
       const int b = blk - BM / 16;
-      src[i] = W + (size_t)min(tn + b * 16 + dr, N - 1) * K + dc;
+      src[i] = W + (size_t)min(tn + b * 16 + dr, N - 1) * K + kbase + dc;
       dst_off[i] = BM * DS_BK + b * 16 * DS_BK;
     }
   }
@@ -334,7 +339,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
     asm volatile("" ::: "memory");
   };
 
-  const int nk = K / DS_BK;
+  const int nk = min(kb_per, K / DS_BK - kb0);
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk) issue(st, st * DS_BK);
@@ -406,7 +411,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
           const float vp = lane_xor1(v);
           if (m < M && n < N && (n & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
         } else if (m < M && n < N) {
-          if (EPI == EPI_STORE_F32) ep.out_f32[(size_t)m * ep.ld + n] = v;
+          if (EPI == EPI_STORE_F32) ep.out_f32[(size_t)blockIdx.y * M * ep.ld + (size_t)m * ep.ld + n] = v;
           else ep.out_f32[(size_t)m * ep.ld + n] += v;
         }
       }
@@ -423,11 +428,15 @@ static constexpr size_t gemm_dma_lds_bytes() {
   return (size_t)NS * (BM + BN) * DS_BK * sizeof(f16_t);
 }
 
+// Returns the number of K slices launched (1 unless split).  A split is aligned to the 64-wide
+// k-steps gemm_splitk_count counts in, so the slice count equals the one it returned.
 template <int BM, int BN, int WGM, int WGN, int NS, bool PIPE = false>
-static void gemm_dma_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep,
-                              hipStream_t s) {
+static int gemm_dma_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep,
+                             hipStream_t s, int splits = 1) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  const dim3 grid(tm * tn);
+  const int nkb = K / DS_BK;
+  const int kb_per = splits > 1 ? 2 * ((((K + 63) / 64) + splits - 1) / splits) : nkb;
+  const dim3 grid(tm * tn, (nkb + kb_per - 1) / kb_per);
   const int nt = 64 * WGM * WGN;
   constexpr size_t lds = gemm_dma_lds_bytes<BM, BN, NS>();
   static bool attr = false;  // above 64 KiB the per-kernel dynamic LDS limit must be raised once
@@ -444,23 +453,24 @@ static void gemm_dma_dispatch(const f16_t* A, const f16_t* W, int M, int N, int 
   }
   switch (ep.kind) {
     case EPI_STORE_F32:
-      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_STORE_F32, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep);
+      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_STORE_F32, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_RESID:
-      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_RESID, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep);
+      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_RESID, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_QKV:
       // The staged RoPE rows (BM x d floats, d <= 128) fit only square 4-stage tiles; other
       // tiles hand the q|k|v projection to the register-staged kernel.
       if constexpr (BM == BN && NS >= 4)
-        launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_QKV, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep);
+        launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_QKV, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       else
         gemm_dispatch<128, 128, 2, 2>(A, W, M, N, K, ep, s);
       break;
     case EPI_SWIGLU:
-      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_SWIGLU, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep);
+      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_SWIGLU, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
   }
+  return (int)grid.y;
 }
 
 template <int BM, int BN>
@@ -567,7 +577,7 @@ size_t gemm_splitk_floats(int M, int N, int K) {
 // Tile choice from a sweep of the Llama-3-8B projection shapes at M = 512, 2048 and
 // 8192 on MI355X.  Shapes with K % 32 == 0 use the LDS-DMA kernel: the 8-wave 256 x 256
 // tile when it still yields at least 192 tiles, 256 x 128 with at least 256, 128 x 128
-// with at least 192, else 64 x 64.  Other K use the register-staged kernel.  Small M
+// with at least 192, else 64 x 64 (tiles no taller than twice the row count).  Other K use the register-staged kernel.  Small M
 // whose tiles cannot fill the GPU is split over K first.
 void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep, float* splitk_ws,
                      size_t splitk_ws_floats, hipStream_t s) {
@@ -582,14 +592,18 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
     pe.kind = EPI_STORE_F32;
     pe.out_f32 = splitk_ws;
     pe.ld = N;
-    gemm_dispatch<64, 64, 2, 2>(a, w, M, N, K, pe, s, sp);
+    int ns = sp;
+    if (K % DS_BK == 0)
+      ns = gemm_dma_dispatch<64, 64, 2, 2, 4>(a, w, M, N, K, pe, s, sp);
+    else
+      gemm_dispatch<64, 64, 2, 2>(a, w, M, N, K, pe, s, sp);
     const size_t n4 = (size_t)M * N / 4;
     const dim3 grid((unsigned)((n4 + 255) / 256));
     switch (ep.kind) {
-      case EPI_STORE_F32: launch_k(splitk_reduce_kernel<EPI_STORE_F32>, grid, 256, 0, s, splitk_ws, sp, M, N, ep); break;
-      case EPI_RESID: launch_k(splitk_reduce_kernel<EPI_RESID>, grid, 256, 0, s, splitk_ws, sp, M, N, ep); break;
-      case EPI_QKV: launch_k(splitk_reduce_kernel<EPI_QKV>, grid, 256, 0, s, splitk_ws, sp, M, N, ep); break;
-      case EPI_SWIGLU: launch_k(splitk_reduce_kernel<EPI_SWIGLU>, grid, 256, 0, s, splitk_ws, sp, M, N, ep); break;
+      case EPI_STORE_F32: launch_k(splitk_reduce_kernel<EPI_STORE_F32>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
+      case EPI_RESID: launch_k(splitk_reduce_kernel<EPI_RESID>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
+      case EPI_QKV: launch_k(splitk_reduce_kernel<EPI_QKV>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
+      case EPI_SWIGLU: launch_k(splitk_reduce_kernel<EPI_SWIGLU>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
     }
     return;
   }
@@ -598,11 +612,11 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
   const bool qkv = ep.kind == EPI_QKV;
   const bool dma_qkv_ok = ep.row_pos == nullptr && ep.head_dim <= 128;
   if (K % DS_BK == 0 && (!qkv || dma_qkv_ok)) {
-    if (tiles(256, 256) >= 192)
+    if (M > 128 && tiles(256, 256) >= 192)
       gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
-    else if (!qkv && tiles(256, 128) >= 256)
+    else if (M > 128 && !qkv && tiles(256, 128) >= 256)
       gemm_dma_dispatch<256, 128, 4, 2, 4>(a, w, M, N, K, ep, s);
-    else if (tiles(128, 128) >= 192)
+    else if (M > 64 && tiles(128, 128) >= 192)
       gemm_dma_dispatch<128, 128, 2, 2, 4>(a, w, M, N, K, ep, s);
     else
       gemm_dma_dispatch<64, 64, 2, 2, 4>(a, w, M, N, K, ep, s);
