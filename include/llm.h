@@ -134,7 +134,9 @@ size_t llm_workspace_bytes(const llm_config* cfg);
  * fp32), build the RoPE cos/sin tables (angle pos * rope_theta^(-2j/head_dim)
  * from an fp64 outer product, "RoPE #1" on the NumPy page) and create a model
  * handle in *out.  The three buffers must stay alive until llm_free; the
- * source weights may be freed once this call returns.  The call synchronises
+ * source weights may be freed once this call returns.  The handle also owns a
+ * small pinned host staging buffer (per-row metadata of llm_prefill_batch), a
+ * capture stream and events, released by llm_free.  The call synchronises
  * `stream` before returning.  Errors: INVALID_ARG (null pointer), CONFIG,
  * BUFFER_TOO_SMALL (a size below the corresponding query), HIP.
  */
@@ -154,6 +156,24 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* weights,
  */
 llm_status llm_prefill(llm_model* m, int32_t slot, const int32_t* tokens_dev, int32_t n_tokens,
                        int32_t start_pos, float* logits_dev, void* stream);
+
+/*
+ * Prefill of several sequences in one call, each as llm_prefill would do it: the
+ * prompt pass of the "Generasi" section applied to a batch of prompts of their own
+ * lengths.  Sequence b has lens_host[b] >= 1 tokens, taken in order from tokens_dev
+ * (device int32, sum of the lengths ids), placed at positions starts_host[b] .. of
+ * cache slot slots_host[b] (positions before starts_host[b] must already be in that
+ * slot's cache).  logits_dev (device fp32 [batch][vocab]) receives the logits of
+ * each sequence's last position.  The three host arrays (batch entries each) are
+ * read during the call; projections run once over all rows, attention per
+ * sequence.  Results equal separate llm_prefill calls up to rounding.  Errors:
+ * INVALID_ARG (null pointer, batch < 1, a length < 1, two sequences with the same
+ * slot), OUT_OF_RANGE (batch > max_batch, a slot >= max_batch, start + length >
+ * max_seq_len, total tokens > max_prefill_tokens), HIP.
+ */
+llm_status llm_prefill_batch(llm_model* m, int32_t batch, const int32_t* slots_host, const int32_t* starts_host,
+                             const int32_t* lens_host, const int32_t* tokens_dev, float* logits_dev,
+                             void* stream);
 
 /*
  * One decoder layer on an explicit residual stream, used to test a layer on its
@@ -222,7 +242,8 @@ enum {
 llm_status llm_set_kernel_timing(llm_model* m, int32_t enable);
 llm_status llm_kernel_timing(llm_model* m, int32_t kind, int64_t* launches, double* total_ms);
 
-/* Release the host-side handle (no device memory is freed). NULL is allowed. */
+/* Release the handle and what it owns on the host (staging buffer, stream,
+ * events, graphs); no caller-provided device memory is freed.  NULL is allowed. */
 void llm_free(llm_model* m);
 
 const char* llm_status_string(llm_status s);

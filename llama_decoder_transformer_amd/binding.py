@@ -26,7 +26,8 @@ STATUS = {0: "LLM_OK", -1: "LLM_ERR_INVALID_ARG", -2: "LLM_ERR_CONFIG", -3: "LLM
 DEVERR_TOKEN, DEVERR_POSITION, DEVERR_SLOT = 1, 2, 4
 
 EXPORTED = ("llm_check_config", "llm_packed_weight_bytes", "llm_kv_cache_bytes", "llm_workspace_bytes",
-            "llm_init_weights", "llm_prefill", "llm_layer_forward", "llm_decode_step", "llm_argmax",
+            "llm_init_weights", "llm_prefill", "llm_prefill_batch", "llm_layer_forward", "llm_decode_step",
+            "llm_argmax",
             "llm_generate", "llm_read_device_error", "llm_set_kernel_timing", "llm_kernel_timing",
             "llm_free", "llm_status_string", "llm_last_error_message")
 KERNEL_GROUPS = ("embed", "rmsnorm", "qkv", "attn", "wo", "gate_up", "down", "lm_head", "argmax")
@@ -77,6 +78,8 @@ def lib():
             "llm_init_weights": (c_int32, [cfgp, POINTER(llm_weights), c_void_p, c_size_t, c_void_p, c_size_t,
                                            c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
             "llm_prefill": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+            "llm_prefill_batch": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_int32), POINTER(c_int32),
+                                            c_void_p, c_void_p, c_void_p]),
             "llm_layer_forward": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p]),
             "llm_decode_step": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
             "llm_argmax": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
@@ -144,6 +147,16 @@ def llm_init_weights(cfg: llm_config, weights: llm_weights, packed, kv_cache, wo
 
 def llm_prefill(handle: int, slot: int, tokens, n_tokens: int, start_pos: int, logits, stream=None) -> None:
     _check(lib().llm_prefill(handle, slot, _ptr(tokens), n_tokens, start_pos, _ptr(logits), _stream(stream)))
+
+
+def llm_prefill_batch(handle: int, slots, starts, lens, tokens, logits, stream=None) -> None:
+    """slots / starts / lens: host integer sequences of equal length (one entry per sequence)."""
+    b = len(lens)
+    if len(slots) != b or len(starts) != b:
+        raise ValueError("slots, starts and lens must have one entry per sequence")
+    arr = c_int32 * max(b, 1)
+    _check(lib().llm_prefill_batch(handle, b, arr(*[int(v) for v in slots]), arr(*[int(v) for v in starts]),
+                                   arr(*[int(v) for v in lens]), _ptr(tokens), _ptr(logits), _stream(stream)))
 
 
 def llm_layer_forward(handle: int, layer: int, slot: int, x, n_tokens: int, start_pos: int, stream=None) -> None:

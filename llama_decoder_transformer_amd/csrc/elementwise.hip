@@ -111,6 +111,20 @@ void launch_pack_rows(const void* src, void* dst, size_t rows, int cols, int row
   launch_k(pack_rows_kernel, blocks, 256, 0, s, (const bf16_t*)src, (f16_t*)dst, rows, cols, row_mult, row_off);
 }
 
+// Gather of whole rows (the last row of each sequence of a batched prefill).
+__global__ void gather_rows_kernel(const float* __restrict__ src, const int* __restrict__ idx, int dim,
+                                   float* __restrict__ dst) {
+  const int i = blockIdx.x;
+  const float* sr = src + (size_t)idx[i] * dim;
+  float* dr = dst + (size_t)i * dim;
+  for (int c = threadIdx.x; c < dim; c += blockDim.x) dr[c] = sr[c];
+}
+
+void launch_gather_rows(const float* src, const int* idx, int n, int dim, float* dst, hipStream_t s) {
+  if (n <= 0) return;
+  launch_k(gather_rows_kernel, n, 256, 0, s, src, idx, dim, dst);
+}
+
 __global__ void fill_i32_kernel(int* p, int v, size_t n) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;

@@ -64,6 +64,8 @@ void launch_to_f32(int dtype, const void* src, float* dst, size_t n, hipStream_t
 void launch_fill_i32(int* p, int v, size_t n, hipStream_t s);
 // bf16 [rows][cols] -> fp16 rows placed at dst row r * row_mult + row_off.
 void launch_pack_rows(const void* src, void* dst, size_t rows, int cols, int row_mult, int row_off, hipStream_t s);
+// dst[i][:] = src[idx[i]][:] for i < n (rows of `dim` floats).
+void launch_gather_rows(const float* src, const int* idx, int n, int dim, float* dst, hipStream_t s);
 // Greedy argmax per row (two passes through `partial`, >= rows*argmax_blocks(vocab)*2 words).
 int argmax_blocks(int vocab);
 void launch_argmax(const float* logits, int rows, int vocab, void* partial, int* out, hipStream_t s);

@@ -85,7 +85,7 @@ struct PackedLayout {
 
 // Workspace layout.
 struct WorkLayout {
-  size_t flags, x, a, q, o, u, attn, amax, splitk, splitk_floats, total;
+  size_t flags, x, a, q, o, u, attn, amax, splitk, splitk_floats, rowmeta, last, total;
   explicit WorkLayout(const llm_config& c) {
     Dims d(c);
     const size_t R = (size_t)d.rows();
@@ -108,6 +108,9 @@ struct WorkLayout {
         for (auto& sh : shapes) splitk_floats = std::max(splitk_floats, gemm_splitk_floats(M, sh[0], sh[1]));
     }
     splitk = p; p = align256(p + splitk_floats * 4);
+    // batched prefill: per-row position and slot, per-sequence last row, gathered last rows
+    rowmeta = p; p = align256(p + (2 * R + (size_t)d.B) * 4);
+    last = p; p = align256(p + (size_t)d.B * d.dim * 4);
     total = p;
   }
 };
@@ -157,6 +160,11 @@ struct llm_model {
   void* amax;
   float* splitk;
   size_t splitk_floats;
+  int* rowmeta;          // device: [R] positions, [R] slots, [B] last-row indices (batched prefill)
+  float* last;           // device: [B][dim] gathered last rows (batched prefill)
+  int* meta_host;        // pinned host staging for rowmeta
+  hipEvent_t meta_ev;    // recorded after the staging copy; waited on before the buffer is refilled
+  bool meta_pending;
   bool mfma_prefill;
   hipStream_t cap_stream;
   std::vector<GraphEntry> graphs;
@@ -281,8 +289,14 @@ void project(llm_model* m, const void* A, const void* W, int M, int N, int K, co
 // One decoder block on M rows of m->x.  Rows are either a prefill run
 // (row_pos == nullptr: positions pos0.., slot slot0) or decode rows with their
 // own positions and slots.
+// One sequence of a batched prefill: rows [row0, row0 + n) of the workspace, positions start..,
+// cache slot `slot`.
+struct SeqSpan {
+  int row0, n, start, slot;
+};
+
 void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_slot, int pos0, int slot0,
-               bool prefill, hipStream_t s) {
+               bool prefill, hipStream_t s, const std::vector<SeqSpan>* seqs = nullptr) {
   const llm_config& c = m->cfg;
   const LayerPtrs& L = m->layers[l];
   const int H = c.n_heads, G = c.n_kv_heads, hd = m->hd, dim = c.dim, F = c.ffn_hidden_dim;
@@ -304,7 +318,12 @@ void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
 
   {
     Timed t(m, LLM_K_ATTN, s);
-    if (prefill && m->mfma_prefill)
+    if (prefill && m->mfma_prefill && seqs) {
+      const size_t rb = (size_t)H * hd * m->es;  // bytes of one q / o row
+      for (const SeqSpan& q : *seqs)
+        launch_attn_prefill((char*)m->q + q.row0 * rb, k_section(m, l), v_section(m, l), q.slot, q.start, q.n, H, G,
+                            hd, c.max_seq_len, (char*)m->o + q.row0 * rb, s);
+    } else if (prefill && m->mfma_prefill && !row_pos)
       launch_attn_prefill(m->q, k_section(m, l), v_section(m, l), slot0, pos0, M, H, G, hd, c.max_seq_len, m->o, s);
     else
       launch_attn_decode(c.dtype, m->q, k_section(m, l), v_section(m, l), row_pos, row_slot, pos0, slot0, M, H, G,
@@ -436,6 +455,11 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   m->amax = ws + wl.amax;
   m->splitk = (float*)(ws + wl.splitk);
   m->splitk_floats = wl.splitk_floats;
+  m->rowmeta = (int*)(ws + wl.rowmeta);
+  m->last = (float*)(ws + wl.last);
+  m->meta_host = nullptr;
+  m->meta_ev = nullptr;
+  m->meta_pending = false;
   m->mfma_prefill = c.dtype == LLM_BF16 && attn_prefill_supported(d.hd, d.H, d.G);
   m->cap_stream = nullptr;
 
@@ -498,6 +522,8 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   if (e == hipSuccess) e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipHostMalloc((void**)&m->meta_host, (2 * (size_t)d.rows() + d.B) * sizeof(int));
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->meta_ev, hipEventDisableTiming);
   if (e != hipSuccess) {
     delete m;
     return fail(LLM_ERR_HIP, std::string("init: ") + hipGetErrorString(e));
@@ -523,6 +549,60 @@ llm_status llm_prefill(llm_model* m, int32_t slot, const int32_t* tokens_dev, in
   for (int l = 0; l < c.n_layers; ++l) run_layer(m, l, n_tokens, nullptr, nullptr, start_pos, slot, true, s);
   lm_head(m, m->x + (size_t)(n_tokens - 1) * c.dim, 1, logits_dev, s);
   return hip_check("prefill launch");
+}
+
+llm_status llm_prefill_batch(llm_model* m, int32_t batch, const int32_t* slots_host, const int32_t* starts_host,
+                             const int32_t* lens_host, const int32_t* tokens_dev, float* logits_dev, void* stream) {
+  if (!m || !slots_host || !starts_host || !lens_host || !tokens_dev || !logits_dev)
+    return fail(LLM_ERR_INVALID_ARG, "NULL model, array or buffer");
+  const llm_config& c = m->cfg;
+  if (batch < 1) return fail(LLM_ERR_INVALID_ARG, "batch must be >= 1");
+  if (batch > c.max_batch) return fail(LLM_ERR_OUT_OF_RANGE, "batch > max_batch");
+  std::vector<SeqSpan> seqs((size_t)batch);
+  std::vector<char> used((size_t)c.max_batch, 0);
+  long long total = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int slot = slots_host[b], start = starts_host[b], n = lens_host[b];
+    if (n < 1) return fail(LLM_ERR_INVALID_ARG, "every sequence needs >= 1 token");
+    if (slot < 0 || slot >= c.max_batch) return fail(LLM_ERR_OUT_OF_RANGE, "slot out of range");
+    if (used[slot]) return fail(LLM_ERR_INVALID_ARG, "two sequences share a slot");
+    used[slot] = 1;
+    if (start < 0 || (long long)start + n > c.max_seq_len)
+      return fail(LLM_ERR_OUT_OF_RANGE, "start + length > max_seq_len");
+    seqs[b] = SeqSpan{(int)total, n, start, slot};
+    total += n;
+  }
+  if (total > c.max_prefill_tokens) return fail(LLM_ERR_OUT_OF_RANGE, "total tokens > max_prefill_tokens");
+  const int T = (int)total;
+  const int R = std::max(c.max_prefill_tokens, c.max_batch);
+  hipStream_t s = as_stream(stream);
+  // Per-row positions and slots and the per-sequence last rows go to the device through the
+  // pinned staging buffer; the previous call's copy must have left it before it is refilled.
+  if (m->meta_pending && hipEventSynchronize(m->meta_ev) != hipSuccess) return hip_check("batched prefill staging");
+  int* hp = m->meta_host;
+  for (const SeqSpan& q : seqs)
+    for (int i = 0; i < q.n; ++i) {
+      hp[q.row0 + i] = q.start + i;
+      hp[R + q.row0 + i] = q.slot;
+    }
+  for (int b = 0; b < batch; ++b) hp[2 * R + b] = seqs[b].row0 + seqs[b].n - 1;
+  int* row_pos = m->rowmeta;
+  int* row_slot = m->rowmeta + R;
+  int* last_idx = m->rowmeta + 2 * R;
+  hipError_t e = hipMemcpyAsync(row_pos, hp, (size_t)T * sizeof(int), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(row_slot, hp + R, (size_t)T * sizeof(int), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(last_idx, hp + 2 * R, (size_t)batch * sizeof(int), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipEventRecord(m->meta_ev, s);
+  if (e != hipSuccess) return fail(LLM_ERR_HIP, std::string("batched prefill staging: ") + hipGetErrorString(e));
+  m->meta_pending = true;
+  {
+    Timed t(m, LLM_K_EMBED, s);
+    launch_embed(c.dtype, m->emb, tokens_dev, T, c.dim, c.vocab_size, m->x, m->flags, s);
+  }
+  for (int l = 0; l < c.n_layers; ++l) run_layer(m, l, T, row_pos, row_slot, 0, 0, true, s, &seqs);
+  launch_gather_rows(m->x, last_idx, batch, c.dim, m->last, s);
+  lm_head(m, m->last, batch, logits_dev, s);
+  return hip_check("batched prefill launch");
 }
 
 llm_status llm_layer_forward(llm_model* m, int32_t layer, int32_t slot, float* x_dev, int32_t n_tokens,
@@ -653,6 +733,11 @@ void llm_free(llm_model* m) {
   for (auto e : m->event_pool) (void)hipEventDestroy(e);
   for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  if (m->meta_ev) {
+    (void)hipEventSynchronize(m->meta_ev);
+    (void)hipEventDestroy(m->meta_ev);
+  }
+  if (m->meta_host) (void)hipHostFree(m->meta_host);
   delete m;
 }
 

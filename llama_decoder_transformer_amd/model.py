@@ -85,6 +85,13 @@ class LlamaModel:
         B.llm_prefill(self.handle, slot, tokens, n, start_pos, logits, stream)
         return logits
 
+    def prefill_batch(self, tokens: torch.Tensor, slots, starts, lens, logits=None, stream=None):
+        """Several prompts at once: tokens holds them back to back; returns [batch, vocab] last-position logits."""
+        if logits is None:
+            logits = torch.empty(len(lens), self.shape.vocab_size, dtype=torch.float32, device=self.device)
+        B.llm_prefill_batch(self.handle, slots, starts, lens, tokens, logits, stream)
+        return logits
+
     def layer_forward(self, layer: int, x: torch.Tensor, slot: int = 0, start_pos: int = 0, stream=None):
         B.llm_layer_forward(self.handle, layer, slot, x, x.shape[0], start_pos, stream)
         return x

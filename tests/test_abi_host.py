@@ -109,6 +109,8 @@ def test_calls_reject_null_handles_and_sizes(B):
     L = B.lib()
     assert L.llm_prefill(None, 0, 256, 4, 0, 256, None) == -1
     assert L.llm_layer_forward(None, 0, 0, 256, 4, 0, None) == -1
+    one = (ctypes.c_int32 * 1)(1)
+    assert L.llm_prefill_batch(None, 1, one, one, one, 256, 256, None) == -1
     assert L.llm_decode_step(None, 1, 256, 256, 256, 256, None) == -1
     assert L.llm_generate(None, 1, 256, 256, 256, 3, 256, 256, None) == -1
     assert L.llm_argmax(None, 1, 10, 256, None) == -1

@@ -336,3 +336,66 @@ def test_llama2_7b_shaped_mha_layer_matches_oracle():
     e = rel_err(got - x, ref - x)
     print(f"[llama2-7b MHA layer S={S}] delta rel err {e:.3e}", flush=True)
     assert e <= TOL_BF16
+
+
+# ---------------------------------------------------------------- batched variable-length prefill
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_batched_prefill_matches_oracle_and_single_prefills(dtype):
+    """Four prompts of different lengths in one call; one of them continues a slot that already
+    holds a prefix (start 40).  Each sequence's logits match the oracle's prefill of that
+    sequence, and the separate single-sequence prefills of the GPU."""
+    if dtype == "bf16":
+        shape, tol, seed = SMALL_BF16, TOL_BF16, 10
+    else:
+        shape, tol, seed = inputs.STORIES15M.replace(max_seq_len=160), TOL_F32, 10
+    hw = host_weights(shape, seed=seed)
+    lens = [150, 1, 37, 64]
+    slots = [2, 0, 3, 1]
+    starts = [0, 0, 40, 0]
+    prompts = [inputs.token_ids(shape.vocab_size, 40 + n, sub=20 + b) for b, n in enumerate(lens)]
+    om = OracleModel(oracle_config(shape), oracle_weights(hw, np.float64))
+    refs = []
+    for b in range(4):
+        full = prompts[b][: starts[b] + lens[b]]
+        refs.append(om.prefill(full)[0])
+    m = _model(shape, hw, max_batch=4, max_prefill=sum(lens))
+    # the slot of sequence 2 already holds its first 40 tokens
+    m.prefill(_i32(prompts[2][:40]), slot=slots[2])
+    toks = np.concatenate([prompts[b][starts[b]: starts[b] + lens[b]] for b in range(4)])
+    lg = m.prefill_batch(_i32(toks), slots, starts, lens).cpu().numpy()
+    errs = [rel_err(lg[b], refs[b]) for b in range(4)]
+    singles = []
+    for b in range(4):
+        one = m.prefill(_i32(prompts[b][starts[b]: starts[b] + lens[b]]), slot=slots[b], start_pos=starts[b])
+        singles.append(rel_err(lg[b], one.cpu().numpy()))
+    print(f"[batched prefill {dtype}] rel errs {np.round(errs, 7).tolist()} vs single {np.round(singles, 7).tolist()}",
+          flush=True)
+    assert max(errs) <= tol and max(singles) <= tol
+    for b in range(4):
+        assert near_tie_ok(int(np.argmax(lg[b])), refs[b], tol)
+    assert m.read_device_error() == 0
+
+
+def test_batched_prefill_rejects_bad_arguments():
+    from llama_decoder_transformer_amd import binding as B
+    shape = SMALL_BF16.replace(n_layers=1)
+    hw = host_weights(shape, seed=11)
+    m = _model(shape, hw, max_batch=2, max_prefill=8)
+    t = _i32([1, 2, 3, 4])
+    with pytest.raises(B.LlmError) as e:
+        m.prefill_batch(t, [0, 0], [0, 0], [2, 2])
+    assert e.value.status == -1  # two sequences share a slot
+    with pytest.raises(B.LlmError) as e:
+        m.prefill_batch(t, [0, 1], [0, 0], [2, 0])
+    assert e.value.status == -1  # empty sequence
+    with pytest.raises(B.LlmError) as e:
+        m.prefill_batch(_i32(list(range(10))), [0, 1], [0, 0], [5, 5])
+    assert e.value.status == -3  # more tokens than max_prefill_tokens
+    with pytest.raises(B.LlmError) as e:
+        m.prefill_batch(t, [0, 1], [shape.max_seq_len - 1, 0], [2, 2])
+    assert e.value.status == -3  # past max_seq_len
+    with pytest.raises(B.LlmError) as e:
+        m.prefill_batch(t, [0, 2], [0, 0], [2, 2])
+    assert e.value.status == -3  # slot out of range
+    assert m.read_device_error() == 0
