@@ -23,6 +23,7 @@
 // N-tile-major: the M tiles that share a weight tile run on the same XCD (one L2)
 // at about the same time and the weights are fetched from HBM once.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "epilogue.h"
@@ -247,7 +248,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int EPI, bool PIPE>
+template <int BM, int BN, int WGM, int WGN, int NS, int EPI, bool SCHED>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* __restrict__ A,
                                                                   const f16_t* __restrict__ W, int M, int N, int K,
                                                                   int tiles_m, int tiles_n, EpiParams ep,
@@ -343,7 +344,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk) issue(st, st * DS_BK);
-  if constexpr (!PIPE) {
+  if constexpr (!SCHED) {
     // Iteration kt: make stage kt visible (NS-2 later stages may still be in flight), refill the
     // buffer of stage kt-1 (every wave finished reading it before this barrier), read and multiply.
     for (int kt = 0; kt < nk; ++kt) {
@@ -353,15 +354,36 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
       mfmas(af[0], bw[0]);
     }
   } else {
-    stage_ready(0, nk, NS - 2);  // stages 1 .. NS-2 issued after stage 0
+    // Scheduled loop.  Fragments are double-buffered in registers: iteration kt makes stage
+    // kt+1 visible, refills the buffer of stage kt-1 (every wave read it before the MFMAs of
+    // iteration kt-1, which precede this barrier), reads stage kt+1's fragments and runs
+    // stage kt's MFMAs.  In the steady state k-steps go in pairs that both issue a real stage
+    // (kt + NS < nk), so the wait before stage kt+1 always allows NS-3 later stages in flight
+    // and the body has no branch: the DMA issue, then the next k-step's fragment reads
+    // interleaved with this k-step's MFMAs by scheduling groups, so the matrix pipe is fed
+    // while the reads are in flight.  The last (at most 4) k-steps run a guarded iteration.
+    // Unrolled by two so the fragment buffers have fixed registers.
+    stage_ready(0, nk, NS - 2);
     read_frags(af[0], bw[0], 0);
-
-    // Iteration kt: make stage kt+1 visible (stages up to kt+NS-2 have been issued, so NS-3 may
-    // still be in flight behind it), refill the buffer of stage kt-1 (every wave read its fragments
-    // before the MFMAs of iteration kt-1, which precede this barrier), read stage kt+1's
-    // fragments, then run stage kt's MFMAs.  Unrolled by two so the fragment buffers have fixed
-    // registers.
-    auto iter = [&](int kt, f16x8_t* a_cur, f16x8_t* b_cur, f16x8_t* a_nxt, f16x8_t* b_nxt) {
+    auto step = [&](int kt, f16x8_t* a_cur, f16x8_t* b_cur, f16x8_t* a_nxt, f16x8_t* b_nxt)
+        __attribute__((always_inline)) {
+      wait_vmcnt<(NS - 3) * PW>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue((kt + NS - 1) % NS, (kt + NS - 1) * DS_BK);
+      read_frags(a_nxt, b_nxt, (kt + 1) % NS);
+      mfmas(a_cur, b_cur);
+      __builtin_amdgcn_sched_group_barrier(0x020, PW, 0);  // DMA first
+#pragma unroll
+      for (int g = 0; g < FM + FN; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      // one fragment read
+        __builtin_amdgcn_sched_group_barrier(0x008, (FM * FN) / (FM + FN), 0);  // then MFMAs
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN) * ((FM * FN) / (FM + FN)), 0);
+    };
+    auto iter = [&](int kt, f16x8_t* a_cur, f16x8_t* b_cur, f16x8_t* a_nxt, f16x8_t* b_nxt)
+        __attribute__((always_inline)) {
       if (kt + 1 < nk) {
         stage_ready(kt + 1, nk, NS - 3);
         if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, (kt + NS - 1) * DS_BK);
@@ -369,11 +391,18 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
       }
       mfmas(a_cur, b_cur);
     };
-    for (int kt = 0; kt < nk; kt += 2) {
-      iter(kt, af[0], bw[0], af[1], bw[1]);
-      if (kt + 1 < nk) iter(kt + 1, af[1], bw[1], af[0], bw[0]);
+    int kt = 0;
+    for (; kt + NS < nk; kt += 2) {
+      step(kt, af[0], bw[0], af[1], bw[1]);
+      step(kt + 1, af[1], bw[1], af[0], bw[0]);
     }
+    static_assert(NS == 4, "the cleanup below covers the last NS k-steps of a 4-stage pipeline");
+    if (kt < nk) iter(kt, af[0], bw[0], af[1], bw[1]);
+    if (kt + 1 < nk) iter(kt + 1, af[1], bw[1], af[0], bw[0]);
+    if (kt + 2 < nk) iter(kt + 2, af[0], bw[0], af[1], bw[1]);
+    if (kt + 3 < nk) iter(kt + 3, af[1], bw[1], af[0], bw[0]);
   }
+
 
   if constexpr (EPI == EPI_QKV) {
     // Prefill rows only (positions pos0 + m, slot slot0, ranges checked by the host, and the
@@ -430,7 +459,7 @@ static constexpr size_t gemm_dma_lds_bytes() {
 
 // Returns the number of K slices launched (1 unless split).  A split is aligned to the 64-wide
 // k-steps gemm_splitk_count counts in, so the slice count equals the one it returned.
-template <int BM, int BN, int WGM, int WGN, int NS, bool PIPE = false>
+template <int BM, int BN, int WGM, int WGN, int NS, bool SCHED = false>
 static int gemm_dma_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep,
                              hipStream_t s, int splits = 1) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
@@ -442,32 +471,32 @@ static int gemm_dma_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K
   static bool attr = false;  // above 64 KiB the per-kernel dynamic LDS limit must be raised once
   if (!attr) {
     attr = true;
-    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_STORE_F32, PIPE>,
+    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_STORE_F32, SCHED>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_RESID, PIPE>,
+    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_RESID, SCHED>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_QKV, PIPE>,
+    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_QKV, SCHED>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_SWIGLU, PIPE>,
+    (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_SWIGLU, SCHED>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   }
   switch (ep.kind) {
     case EPI_STORE_F32:
-      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_STORE_F32, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_STORE_F32, SCHED>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_RESID:
-      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_RESID, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_RESID, SCHED>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_QKV:
       // The staged RoPE rows (BM x d floats, d <= 128) fit only square 4-stage tiles; other
       // tiles hand the q|k|v projection to the register-staged kernel.
       if constexpr (BM == BN && NS >= 4)
-        launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_QKV, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+        launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_QKV, SCHED>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       else
         gemm_dispatch<128, 128, 2, 2>(A, W, M, N, K, ep, s);
       break;
     case EPI_SWIGLU:
-      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_SWIGLU, PIPE>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_SWIGLU, SCHED>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
   }
   return (int)grid.y;
@@ -615,7 +644,7 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
     if (M > 128 && tiles(256, 256) >= 192)
       gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
     else if (M > 128 && !qkv && tiles(256, 128) >= 256)
-      gemm_dma_dispatch<256, 128, 4, 2, 4>(a, w, M, N, K, ep, s);
+      gemm_dma_dispatch<256, 128, 4, 2, 4, true>(a, w, M, N, K, ep, s);
     else if (M > 64 && tiles(128, 128) >= 192)
       gemm_dma_dispatch<128, 128, 2, 2, 4>(a, w, M, N, K, ep, s);
     else
