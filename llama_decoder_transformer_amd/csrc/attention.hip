@@ -264,46 +264,56 @@ __global__ void __launch_bounds__(NT) attn_decode_kernel(const T* __restrict__ q
 }
 
 // Merge the chunk partials of one (row, head) when the row spans several chunks:
-// o = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M), M = max_c m_c.
+// o = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M), M = max_c m_c, as a running merge over
+// rounds of CB chunks.  Thread e owns output element e.  The first round's loads do not
+// depend on the row's position (a chunk past the row's last is loaded and then ignored), so
+// they are in flight together with the position load: one memory round trip for short rows.
 template <typename T, int D>
 __global__ void __launch_bounds__(128) attn_combine_kernel(const float* __restrict__ partial,
                                                            const int* __restrict__ row_pos,
                                                            const int* __restrict__ row_slot, int pos0, int slot0,
                                                            int H, int max_seq, int n_slots, int CH, int nchunks,
                                                            T* __restrict__ out) {
-  const int h = blockIdx.x, row = blockIdx.y;
+  constexpr int CB = 8;
+  const int h = blockIdx.x, row = blockIdx.y, e = threadIdx.x;
+  const float* pr = partial + ((size_t)row * H + h) * nchunks * (D + 2);
+  float mc[CB], lc[CB], ac[CB];
+  auto load_round = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int c = c0 + j;
+      mc[j] = -1e30f;
+      lc[j] = 0.f;
+      ac[j] = 0.f;
+      if (c < nchunks) {
+        mc[j] = pr[(size_t)c * (D + 2) + D];
+        lc[j] = pr[(size_t)c * (D + 2) + D + 1];
+        if (e < D) ac[j] = pr[(size_t)c * (D + 2) + e];
+      }
+    }
+  };
+  load_round(0);
   const int pos = row_pos ? row_pos[row] : pos0 + row;
   const int slot = row_slot ? row_slot[row] : slot0;
   if (pos < 0 || pos >= max_seq || slot < 0 || slot >= n_slots) return;
   const int nv = pos / CH + 1;
   if (nv == 1) return;
-  const float* pr = partial + ((size_t)row * H + h) * nchunks * (D + 2);
-  extern __shared__ float s_w[];  // [nchunks] chunk weights
-  __shared__ float s_inv;
-  // chunk weights 2^(m_c - M) and 1 / L, computed by the first wave
-  if (threadIdx.x < 64) {
-    float mc = -1e30f, lc = 0.f;
-    for (int c = threadIdx.x; c < nv; c += 64) {
-      mc = fmaxf(mc, pr[(size_t)c * (D + 2) + D]);
+  float m = -1e30f, l = 0.f, a = 0.f;
+  for (int c0 = 0;; c0 += CB) {
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      if (c0 + j < nv) {
+        const float mn = fmaxf(m, mc[j]);
+        const float s0 = exp2f(m - mn), s1 = exp2f(mc[j] - mn);
+        l = l * s0 + lc[j] * s1;
+        a = a * s0 + ac[j] * s1;
+        m = mn;
+      }
     }
-    const float M = wave_max(mc);
-    float L = 0.f;
-    for (int c = threadIdx.x; c < nv; c += 64) {
-      const float w = exp2f(pr[(size_t)c * (D + 2) + D] - M);
-      lc = pr[(size_t)c * (D + 2) + D + 1];
-      s_w[c] = w;
-      L += w * lc;
-    }
-    L = wave_sum(L);
-    if (threadIdx.x == 0) s_inv = 1.0f / L;
+    if (c0 + CB >= nv) break;
+    load_round(c0 + CB);
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < D; e += 128) {
-    float a = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < nv; ++c) a += pr[(size_t)c * (D + 2) + e] * s_w[c];
-    out[(size_t)row * H * D + (size_t)h * D + e] = from_f32<T>(a * s_inv);
-  }
+  if (e < D) out[(size_t)row * H * D + (size_t)h * D + e] = from_f32<T>(a / l);
 }
 
 int attn_decode_chunk(int rows, int n_kv_heads, int max_seq) {
@@ -355,7 +365,7 @@ static void attn_decode_dispatch(const T* q, const T* kc, const T* vc, const int
   launch_k(attn_decode_kernel<T, D, 256, DEC_MAXH>, grid, 256, 0, s, q, kc, vc, row_pos, row_slot, pos0, slot0, H, G,
                                                               max_seq, n_slots, CH, nch, hpb, partial, out, err);
   if (nch > 1)
-    launch_k(attn_combine_kernel<T, D>, dim3(H, rows), 128, nch * sizeof(float), s, partial, row_pos, row_slot, pos0, slot0,
+    launch_k(attn_combine_kernel<T, D>, dim3(H, rows), 128, 0, s, partial, row_pos, row_slot, pos0, slot0,
                                                                             H, max_seq, n_slots, CH, nch, out);
 }
 
@@ -853,7 +863,7 @@ static bool attn_decode_mfma(const f16_t* q, const f16_t* kc, const f16_t* vc, c
   launch_k(attn_decode_mfma_kernel<4>, dim3(nch, G, rows), 256, 0, s, q, kc, vc, row_pos, row_slot, pos0, slot0, H, G, max_seq,
                                                              n_slots, CH, nch, partial, out, err);
   if (nch > 1)
-    launch_k(attn_combine_kernel<f16_t, PF_D>, dim3(H, rows), 128, nch * sizeof(float), s, 
+    launch_k(attn_combine_kernel<f16_t, PF_D>, dim3(H, rows), 128, 0, s, 
         partial, row_pos, row_slot, pos0, slot0, H, max_seq, n_slots, CH, nch, out);
   return true;
 }

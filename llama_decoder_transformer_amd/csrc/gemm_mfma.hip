@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
   constexpr int NI = (BM + BN) / 16;        // DMA instructions per stage
   constexpr int PW = NI / NW;               // ... per wave
   static_assert(NI % NW == 0, "DMA instructions do not split evenly over the waves");
-  static_assert(NS >= 3 && NS <= 5, "stages");
+  static_assert(NS >= 3 && NS <= 8 && (NS - 2) * PW < 64, "stages");
 
   extern __shared__ __attribute__((aligned(16))) f16_t smem[];
 
@@ -330,10 +330,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
   // waited for its own part and passed the barrier, the stage is in LDS.
   auto stage_ready = [&](int st, int nk, int depth) {
     const int later = min(depth, nk - 1 - st);
-    if (later >= 3) wait_vmcnt<3 * PW>();
-    else if (later == 2) wait_vmcnt<2 * PW>();
-    else if (later == 1) wait_vmcnt<PW>();
-    else wait_vmcnt<0>();
+    switch (later) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<PW>(); break;
+      case 2: wait_vmcnt<2 * PW>(); break;
+      case 3: wait_vmcnt<3 * PW>(); break;
+      case 4: wait_vmcnt<4 * PW>(); break;
+      case 5: wait_vmcnt<5 * PW>(); break;
+      default: wait_vmcnt<6 * PW>(); break;
+    }
     // A bare barrier: __syncthreads() would add a release fence that waits for all loads in flight.
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -640,7 +645,9 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
   // fit its stage buffers: BM = BN square tiles with 4 stages hold d <= 128.
   const bool qkv = ep.kind == EPI_QKV;
   const bool dma_qkv_ok = ep.row_pos == nullptr && ep.head_dim <= 128;
-  if (K % DS_BK == 0 && (!qkv || dma_qkv_ok)) {
+  // At M <= 64 (weight streaming, e.g. a batch's LM head) the register-staged kernel's 64-wide
+  // K steps measured faster than the DMA kernel's 32-wide ones.
+  if (M > 64 && K % DS_BK == 0 && (!qkv || dma_qkv_ok)) {
     if (M > 128 && tiles(256, 256) >= 192)
       gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
     else if (M > 128 && !qkv && tiles(256, 128) >= 256)
