@@ -129,6 +129,31 @@ def test_llama3_8b_layer_2048_matches_oracle():
     assert e <= TOL_BF16 and e_delta <= TOL_BF16
 
 
+@pytest.mark.parametrize("S,start", [(300, 0), (523, 97)])
+def test_llama3_8b_layer_ragged_rows_match_oracle(S, start):
+    """Llama-3-8B-shaped layer with row counts that leave partial 256-row tiles (the gate-up
+    projection takes the 256 x 256 tile), once from position 0 and once continuing a cache that
+    already holds `start` positions (rows of the RoPE table staged from an offset)."""
+    shape = inputs.WORKLOADS["llama3-8b-layer"].shape.replace(vocab_size=256)
+    hw = host_weights(shape, seed=12)
+    m = _model(shape, hw, max_batch=1, max_prefill=max(S, start))
+    om = OracleModel(oracle_config(shape), oracle_weights(hw, np.float32))
+    cache = om.new_cache(start + S)
+    if start:
+        x0 = inputs.bf16_bits_to_f32(inputs.activations_bf16_bits(start, shape.dim, seed=start))
+        m.layer_forward(0, torch.from_numpy(x0.copy()).to(DEV))
+        om.layer(0, x0.astype(np.float64), cache, np.arange(start))
+    x = inputs.bf16_bits_to_f32(inputs.activations_bf16_bits(S, shape.dim, seed=S))
+    xd = torch.from_numpy(x.copy()).to(DEV)
+    m.layer_forward(0, xd, start_pos=start)
+    got = xd.cpu().numpy()
+    del m
+    ref = om.layer(0, x.astype(np.float64), cache, np.arange(start, start + S))
+    e = rel_err(got - x, ref - x)
+    print(f"[8b layer S={S} start={start}] delta rel err {e:.3e}", flush=True)
+    assert e <= TOL_BF16
+
+
 def test_small_bf16_model_prefill_then_decode_teacher_forced():
     shape = SMALL_BF16
     hw = host_weights(shape, seed=1)
