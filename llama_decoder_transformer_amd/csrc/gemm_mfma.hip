@@ -603,16 +603,54 @@ int gemm_splitk_count(int M, int N, int K) {
   return (nkb + per - 1) / per;
 }
 
-size_t gemm_splitk_floats(int M, int N, int K) {
-  const int sp = gemm_splitk_count(M, N, K);
-  return sp > 1 ? (size_t)sp * M * N : 0;
+// Prefill row counts (M > 128) whose large tiles cannot fill the GPU: 256 x 256 tiles when they
+// number at least 192, else 256 x 128 (not for the q|k|v epilogue, which needs square tiles)
+// when they do; otherwise K is split over the 256 x 256 or 256 x 128 tiles with at least 1024
+// k per slice and at most 320 workgroups, taking the most workgroups up to 256, then the fewest
+// slices, then the larger tile.  From a sweep of the Llama-3-8B projections at M = 256, 512
+// and 1024 on MI355X (e.g. down at M = 512: 498 TFLOP/s unsplit on 64 x 64 tiles, 841 on
+// 256 x 128 tiles in 4 slices, the partial sums included).
+struct BigPlan {
+  int tile;  // 0: 256 x 256, 1: 256 x 128
+  int splits;
+};
+
+static bool big_tile_plan(int M, int N, int K, bool qkv, BigPlan& p) {
+  if (M <= 128 || K % DS_BK != 0) return false;
+  auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (tiles(256, 256) >= 192) { p = {0, 1}; return true; }
+  if (!qkv && tiles(256, 128) >= 192) { p = {1, 1}; return true; }
+  long best = 0;
+  bool found = false;
+  for (int sp = 2; sp <= 8; sp *= 2) {
+    if (K / sp < 1024 || N % 4 != 0) break;
+    for (int t = 0; t < 2; ++t) {
+      const long wg = tiles(256, t == 0 ? 256 : 128) * sp;
+      if (wg > 320) continue;
+      const long score = std::min<long>(wg, 256);
+      if (!found || score > best) { best = score; p = {t, sp}; found = true; }
+    }
+  }
+  return found;
 }
 
-// Tile choice from a sweep of the Llama-3-8B projection shapes at M = 512, 2048 and
-// 8192 on MI355X.  Shapes with K % 32 == 0 use the LDS-DMA kernel: the 8-wave 256 x 256
-// tile when it still yields at least 192 tiles, 256 x 128 with at least 256, 128 x 128
-// with at least 192, else 64 x 64 (tiles no taller than twice the row count).  Other K use the register-staged kernel.  Small M
-// whose tiles cannot fill the GPU is split over K first.
+size_t gemm_splitk_floats(int M, int N, int K) {
+  BigPlan bp;
+  // The q|k|v projection is the only one with N = (H + 2 G) d; which projection it is matters
+  // only for the tile choice, so both readings are sized for.
+  size_t need = 0;
+  for (bool qkv : {false, true})
+    if (big_tile_plan(M, N, K, qkv, bp) && bp.splits > 1) need = std::max(need, (size_t)bp.splits * M * N);
+  const int sp = gemm_splitk_count(M, N, K);
+  if (sp > 1) need = std::max(need, (size_t)sp * M * N);
+  return need;
+}
+
+// Tile choice from sweeps of the Llama-3-8B projection shapes at M = 256 .. 8192 on MI355X.
+// Shapes with K % 32 == 0 use the LDS-DMA kernel: M <= 128 split over K on 64 x 64 tiles
+// (gemm_splitk_count); larger M as big_tile_plan says (256 x 256 or 256 x 128 tiles, split
+// over K when they are too few), then 128 x 128 with at least 192 tiles, else 64 x 64.  Other
+// K use the register-staged kernel.
 void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep, float* splitk_ws,
                      size_t splitk_ws_floats, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
@@ -620,6 +658,30 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
   const f16_t* a = (const f16_t*)A;
   const f16_t* w = (const f16_t*)W;
   auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  auto reduce = [&](int ns) {
+    const size_t n4 = (size_t)M * N / 4;
+    const dim3 grid((unsigned)((n4 + 255) / 256));
+    switch (ep.kind) {
+      case EPI_STORE_F32: launch_k(splitk_reduce_kernel<EPI_STORE_F32>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
+      case EPI_RESID: launch_k(splitk_reduce_kernel<EPI_RESID>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
+      case EPI_QKV: launch_k(splitk_reduce_kernel<EPI_QKV>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
+      case EPI_SWIGLU: launch_k(splitk_reduce_kernel<EPI_SWIGLU>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
+    }
+  };
+  {
+    BigPlan bp;
+    if (big_tile_plan(M, N, K, ep.kind == EPI_QKV, bp) && bp.splits > 1 && splitk_ws &&
+        (size_t)bp.splits * M * N <= splitk_ws_floats) {
+      EpiParams pe = ep;
+      pe.kind = EPI_STORE_F32;
+      pe.out_f32 = splitk_ws;
+      pe.ld = N;
+      const int ns = bp.tile == 0 ? gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, pe, s, bp.splits)
+                                  : gemm_dma_dispatch<256, 128, 4, 2, 4, true>(a, w, M, N, K, pe, s, bp.splits);
+      reduce(ns);
+      return;
+    }
+  }
   const int sp = gemm_splitk_count(M, N, K);
   if (sp > 1 && splitk_ws && (size_t)sp * M * N <= splitk_ws_floats) {
     EpiParams pe = ep;
@@ -631,14 +693,7 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
       ns = gemm_dma_dispatch<64, 64, 2, 2, 4>(a, w, M, N, K, pe, s, sp);
     else
       gemm_dispatch<64, 64, 2, 2>(a, w, M, N, K, pe, s, sp);
-    const size_t n4 = (size_t)M * N / 4;
-    const dim3 grid((unsigned)((n4 + 255) / 256));
-    switch (ep.kind) {
-      case EPI_STORE_F32: launch_k(splitk_reduce_kernel<EPI_STORE_F32>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
-      case EPI_RESID: launch_k(splitk_reduce_kernel<EPI_RESID>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
-      case EPI_QKV: launch_k(splitk_reduce_kernel<EPI_QKV>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
-      case EPI_SWIGLU: launch_k(splitk_reduce_kernel<EPI_SWIGLU>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
-    }
+    reduce(ns);
     return;
   }
   // The DMA kernel's q|k|v epilogue handles prefill rows whose RoPE table rows (BM x d floats)
@@ -650,7 +705,7 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
   if (M > 64 && K % DS_BK == 0 && (!qkv || dma_qkv_ok)) {
     if (M > 128 && tiles(256, 256) >= 192)
       gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
-    else if (M > 128 && !qkv && tiles(256, 128) >= 256)
+    else if (M > 128 && !qkv && tiles(256, 128) >= 192)
       gemm_dma_dispatch<256, 128, 4, 2, 4, true>(a, w, M, N, K, ep, s);
     else if (M > 64 && tiles(128, 128) >= 192)
       gemm_dma_dispatch<128, 128, 2, 2, 4>(a, w, M, N, K, ep, s);

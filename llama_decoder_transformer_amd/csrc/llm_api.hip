@@ -100,11 +100,11 @@ struct WorkLayout {
     u = p; p = align256(p + R * d.F * d.es);
     attn = p; p = align256(p + attn_decode_partial_floats(att_rows, d.H, d.hd, d.S) * 4);
     amax = p; p = align256(p + (size_t)d.B * argmax_blocks(d.V) * 8);
-    // split-K partials of the MFMA projections at small row counts
+    // split-K partials of the MFMA projections at row counts whose tiles cannot fill the GPU
     splitk_floats = 0;
     if (c.dtype == LLM_BF16) {
       const int shapes[4][2] = {{d.qkv_rows(), d.dim}, {d.dim, d.H * d.hd}, {2 * d.F, d.dim}, {d.dim, d.F}};
-      for (int M = 9; M <= (int)std::min<size_t>(R, 128); ++M)
+      for (int M = 9; M <= (int)R; ++M)
         for (auto& sh : shapes) splitk_floats = std::max(splitk_floats, gemm_splitk_floats(M, sh[0], sh[1]));
     }
     splitk = p; p = align256(p + splitk_floats * 4);
