@@ -74,6 +74,38 @@ __device__ __forceinline__ void epi_qkv(const EpiParams& p, int m, int n, float 
   qkv_store<TA>(p, qkv_prepare(p, m, n), m, n, v, vp);
 }
 
+// Four consecutive columns n .. n + 3 of one row (n % 4 == 0, head_dim % 4 == 0): they share
+// the role (q, k or v), head and row, hold RoPE pairs (n, n + 1) and (n + 2, n + 3), and land
+// in 4 consecutive fp16 elements of the destination, written as one 8-byte store.
+__device__ __forceinline__ void qkv_store4(const EpiParams& p, int m, int n, const float (&a)[4]) {
+  int pos, slot;
+  if (!epi_row(p, m, pos, slot)) return;
+  const int d = p.head_dim;
+  const int qd = p.n_heads * d, kd = p.n_kv_heads * d;
+  const int kind = n < qd ? 0 : (n < qd + kd ? 1 : 2);
+  const int col = kind == 0 ? n : (kind == 1 ? n - qd : n - qd - kd);
+  const int g = col / d, e = col - g * d;
+  float r[4] = {a[0], a[1], a[2], a[3]};
+  if (kind < 2) {
+    const size_t t = (size_t)pos * (d >> 1) + (e >> 1);
+    const float2 c = *reinterpret_cast<const float2*>(p.rope_cos + t);
+    const float2 s = *reinterpret_cast<const float2*>(p.rope_sin + t);
+    r[0] = a[0] * c.x - a[1] * s.x;
+    r[1] = a[1] * c.x + a[0] * s.x;
+    r[2] = a[2] * c.y - a[3] * s.y;
+    r[3] = a[3] * c.y + a[2] * s.y;
+  }
+  f16_t* dst = kind == 0 ? reinterpret_cast<f16_t*>(p.out_act) + (size_t)m * p.ld + n
+                         : reinterpret_cast<f16_t*>(kind == 1 ? p.k_cache : p.v_cache) +
+                               (((size_t)slot * p.n_kv_heads + g) * p.max_seq + pos) * d + e;
+  f16x2_t lo, hi;
+  lo.x = (f16_t)r[0];
+  lo.y = (f16_t)r[1];
+  hi.x = (f16_t)r[2];
+  hi.y = (f16_t)r[3];
+  *reinterpret_cast<uint2*>(dst) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // q|k|v epilogue of an MFMA tile held as acc[FM][FN] (16 x 16 blocks; this lane holds rows
 // m_base + 16 i + 4 lg + r of column n_base + 16 jn + l16).  The column's role (q, k or v),
 // head, RoPE pair, destination base and row stride depend only on the column, so they are

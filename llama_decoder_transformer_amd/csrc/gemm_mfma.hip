@@ -579,6 +579,10 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
   }
   const float a[4] = {v.x, v.y, v.z, v.w};
+  if (EPI == EPI_QKV && (ep.head_dim & 3) == 0) {
+    qkv_store4(ep, m, n, a);
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     if (EPI == EPI_STORE_F32) ep.out_f32[(size_t)m * ep.ld + n + c] = a[c];
