@@ -593,14 +593,18 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
 }
 
 // Number of K splits for a GEMM: only small-M shapes (weight streaming) whose 64 x 64
-// tiles give fewer than 1024 workgroups are split, aiming at about 1024 workgroups, at
-// most 8 splits and at least 4 K steps of 64 per split.
+// tiles give fewer than 256 workgroups (one per CU) are split: the smallest power of two
+// giving at least 384 of them, at most 8 and at least 4 K steps of 64 per split.  From a sweep
+// at M = 16, 64 and 128 on MI355X with the weights streamed from HBM (rotating copies): at 64
+// rows, q|k|v streams at 3.1 TB/s in 4 slices, wo at 2.5 in 4 or 8, down at 3.8 in 8 (on
+// 64 x 128 tiles), while the 448-tile gate-up projection is fastest unsplit.
 int gemm_splitk_count(int M, int N, int K) {
   if (M <= 0 || M > 128 || N % 4 != 0) return 1;
   const long tiles = (long)((M + 63) / 64) * ((N + 63) / 64);
-  if (tiles >= 1024) return 1;
+  if (tiles >= 256) return 1;
   const int nkb = (K + GEMM_BK - 1) / GEMM_BK;
-  int sp = (int)std::min<long>(8, (1024 + tiles - 1) / tiles);
+  int sp = 2;
+  while (sp < 8 && tiles * sp < 384) sp *= 2;
   sp = std::min(sp, nkb / 4);
   if (sp < 2) return 1;
   const int per = (nkb + sp - 1) / sp;
@@ -693,7 +697,9 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
     pe.out_f32 = splitk_ws;
     pe.ld = N;
     int ns = sp;
-    if (K % DS_BK == 0)
+    if (K % DS_BK == 0 && K >= 8192)  // long rows (down): 64 x 128 tiles, 3.8 TB/s against 3.2
+      ns = gemm_dma_dispatch<64, 128, 1, 4, 4>(a, w, M, N, K, pe, s, sp);
+    else if (K % DS_BK == 0)
       ns = gemm_dma_dispatch<64, 64, 2, 2, 4>(a, w, M, N, K, pe, s, sp);
     else
       gemm_dispatch<64, 64, 2, 2>(a, w, M, N, K, pe, s, sp);
@@ -704,8 +710,22 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
   // fit its stage buffers: BM = BN square tiles with 4 stages hold d <= 128.
   const bool qkv = ep.kind == EPI_QKV;
   const bool dma_qkv_ok = ep.row_pos == nullptr && ep.head_dim <= 128;
-  // At M <= 64 (weight streaming, e.g. a batch's LM head) the register-staged kernel's 64-wide
-  // K steps measured faster than the DMA kernel's 32-wide ones.
+  // Unsplit row counts up to 128 stream the weights, and wider tiles re-read the activations
+  // less: at most 64 rows, 64 x 128 tiles when there are 256 to 1024 of 64 x 64 (gate-up: 4.3
+  // TB/s against 3.5 on 64 x 64 tiles); above 64 rows, 64 x 256 tiles when they number 192 to
+  // 512 (gate-up at 128 rows: 3.2 TB/s against 2.7).  Wider N (a batch's LM head) stays on the
+  // register-staged 64 x 64 kernel up to 64 rows (5.2 TB/s) and on 128 x 128 tiles above.
+  if (M <= 128 && K % DS_BK == 0 && !qkv) {
+    const long t64 = tiles(64, 64), t256 = tiles(64, 256);
+    if (M <= 64 && t64 >= 256 && t64 <= 1024) {
+      gemm_dma_dispatch<64, 128, 1, 4, 4>(a, w, M, N, K, ep, s);
+      return;
+    }
+    if (M > 64 && t256 >= 192 && t256 <= 512) {
+      gemm_dma_dispatch<64, 256, 1, 4, 4>(a, w, M, N, K, ep, s);
+      return;
+    }
+  }
   if (M > 64 && K % DS_BK == 0 && (!qkv || dma_qkv_ok)) {
     if (M > 128 && tiles(256, 256) >= 192)
       gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
