@@ -129,11 +129,12 @@ def test_llama3_8b_layer_2048_matches_oracle():
     assert e <= TOL_BF16 and e_delta <= TOL_BF16
 
 
-@pytest.mark.parametrize("S,start", [(300, 0), (523, 97)])
+@pytest.mark.parametrize("S,start", [(300, 0), (523, 97), (100, 0), (64, 13)])
 def test_llama3_8b_layer_ragged_rows_match_oracle(S, start):
-    """Llama-3-8B-shaped layer with row counts that leave partial 256-row tiles (the gate-up
-    projection takes the 256 x 256 tile), once from position 0 and once continuing a cache that
-    already holds `start` positions (rows of the RoPE table staged from an offset)."""
+    """Llama-3-8B-shaped layer with row counts that leave partial tiles: 300 and 523 rows (256 x 256
+    gate-up tiles, K split over 256 x 128 tiles for the others), 100 rows (64 x 256 gate-up tiles,
+    64-row split-K tiles) and 64 rows (64 x 128 gate-up tiles); from position 0 or continuing a
+    cache that already holds `start` positions (rows of the RoPE table staged from an offset)."""
     shape = inputs.WORKLOADS["llama3-8b-layer"].shape.replace(vocab_size=256)
     hw = host_weights(shape, seed=12)
     m = _model(shape, hw, max_batch=1, max_prefill=max(S, start))
