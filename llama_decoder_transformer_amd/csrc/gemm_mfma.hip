@@ -5,6 +5,11 @@
 // are rounded to fp16 rather than bf16: same bytes and MFMA rate, 8x finer
 // rounding, which keeps 32 layers within the bf16 parity bar.
 //
+// Two kernels share the tiling, fragment layout and epilogues: gemm_dma_kernel (the LDS-DMA
+// pipeline further below) serves every K % 32 == 0 shape but a batch's LM head, and the
+// register-staged gemm_f16_kernel described here serves the rest.  launch_gemm_f16 at the
+// end of the file picks tiles and K splits per shape.
+//
 // Tiling: BM x BN output tile per 256-thread workgroup (4 waves as 2 x 2, each
 // owning a BM/2 x BN/2 sub-tile), BK = 64 per stage, v_mfma_f32_16x16x32_f16 on
 // 16x16 blocks.  A lane feeds row (lane % 16) and the 8 k-values starting at
@@ -40,7 +45,7 @@ constexpr int GEMM_LDK = GEMM_BK;  // LDS row = 128 bytes = 8 chunks of 16 bytes
 // each) hit distinct banks.
 __device__ __forceinline__ int lds_off(int r, int c) { return r * GEMM_LDK + ((c ^ ((r >> 1) & 7)) << 3); }
 
-template <int BM, int BN, int WGM, int WGN, int EPI, int NPART = 1, bool SB = false>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool SB = false>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* __restrict__ A,
                                                                   const f16_t* __restrict__ W, int M, int N, int K,
                                                                   int tiles_m, int tiles_n, EpiParams ep,
@@ -70,19 +75,17 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
   const int wm = wid / WGN, wn = wid % WGN;
   const int l16 = lane & 15, lg = lane >> 4;
 
-  // The next stage's global loads are split into NPART parts, one per k-step of
-  // 32, so only 1/NPART of a stage sits in registers at a time.
-  static_assert((BK / 32) % NPART == 0 && A_LD % NPART == 0 && B_LD % NPART == 0, "bad NPART");
-  constexpr int PA = A_LD / NPART, PB = B_LD / NPART;
+  // The next stage's global loads sit in registers while the current stage is multiplied.
+  constexpr int PA = A_LD, PB = B_LD;
   u32x4_t ra[PA], rb[PB];
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
   // Out-of-range rows / columns load from a clamped in-range address and are then
   // replaced by zero with a select, so the loads stay branch-free.
-  auto gload = [&](int k0, int part) {
+  auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
-      const int idx = tid + (part * PA + i) * NT, r = idx >> 3, c = (idx & 7) * 8;
+      const int idx = tid + i * NT, r = idx >> 3, c = (idx & 7) * 8;
       const int gm = tm + r, gk = k0 + c;
       const bool ok = gm < M && gk < K;
       const u32x4_t v =
@@ -91,7 +94,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
     }
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const int idx = tid + (part * PB + i) * NT, r = idx >> 3, c = (idx & 7) * 8;
+      const int idx = tid + i * NT, r = idx >> 3, c = (idx & 7) * 8;
       const int gn = tn + r, gk = k0 + c;
       const bool ok = gn < N && gk < K;
       const u32x4_t v =
@@ -99,17 +102,17 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
       rb[i] = ok ? v : zero;
     }
   };
-  auto sstore = [&](int stage, int part) {
+  auto sstore = [&](int stage) {
     f16_t* As = smem + stage * STAGE;
     f16_t* Bs = As + BM * LDK;
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
-      const int idx = tid + (part * PA + i) * NT, r = idx >> 3, c = (idx & 7) * 8;
+      const int idx = tid + i * NT, r = idx >> 3, c = (idx & 7) * 8;
       *reinterpret_cast<u32x4_t*>(&As[lds_off(r, c >> 3)]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const int idx = tid + (part * PB + i) * NT, r = idx >> 3, c = (idx & 7) * 8;
+      const int idx = tid + i * NT, r = idx >> 3, c = (idx & 7) * 8;
       *reinterpret_cast<u32x4_t*>(&Bs[lds_off(r, c >> 3)]) = rb[i];
     }
   };
@@ -124,11 +127,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
   const int kb0 = blockIdx.y * kb_per;
   const int nk = min(kb_per, (K + BK - 1) / BK - kb0);
   const int kbase = kb0 * BK;
-#pragma unroll
-  for (int part = 0; part < NPART; ++part) {
-    gload(kbase, part);
-    sstore(0, part);
-  }
+  gload(kbase);
+  sstore(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
@@ -137,8 +137,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
     const f16_t* Bs = As + BM * LDK;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      constexpr int KS_PER_PART = (BK / 32) / NPART;
-      if (more && ks % KS_PER_PART == 0) gload(kbase + (kt + 1) * BK, ks / KS_PER_PART);
+      if (more && ks == 0) gload(kbase + (kt + 1) * BK);
       f16x8_t af[FM], bw[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -154,7 +153,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
 #pragma unroll
         for (int jn = 0; jn < FN; ++jn)
           acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bw[jn], acc[i][jn], 0, 0, 0);
-      if (more && ks % KS_PER_PART == KS_PER_PART - 1) sstore(cur ^ 1, ks / KS_PER_PART);
+      if (more && ks == BK / 32 - 1) sstore(cur ^ 1);
     }
     __syncthreads();
   }
@@ -453,7 +452,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NPART = 1, bool SB = false>
+template <int BM, int BN, int WGM, int WGN, bool SB = false>
 static void gemm_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep, hipStream_t s,
                           int splits = 1);
 
@@ -512,7 +511,7 @@ static size_t gemm_lds_bytes() {
   return (size_t)2 * (BM + BN) * GEMM_LDK * sizeof(f16_t);
 }
 
-template <int BM, int BN, int WGM, int WGN, int NPART, bool SB>
+template <int BM, int BN, int WGM, int WGN, bool SB>
 static void gemm_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep, hipStream_t s,
                           int splits) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
@@ -523,30 +522,30 @@ static void gemm_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, c
   const size_t lds = gemm_lds_bytes<BM, BN>();
   switch (ep.kind) {
     case EPI_STORE_F32:
-      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_STORE_F32, NPART, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_STORE_F32, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_RESID:
-      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_RESID, NPART, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_RESID, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_QKV:
-      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_QKV, NPART, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_QKV, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_SWIGLU:
-      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_SWIGLU, NPART, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      launch_k(gemm_f16_kernel<BM, BN, WGM, WGN, EPI_SWIGLU, SB>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NPART = 1, bool SB = false>
+template <int BM, int BN, int WGM, int WGN, bool SB = false>
 static void gemm_set_lds_limit() {
   const int bytes = (int)gemm_lds_bytes<BM, BN>();
-  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_STORE_F32, NPART, SB>,
+  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_STORE_F32, SB>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_RESID, NPART, SB>,
+  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_RESID, SB>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_QKV, NPART, SB>,
+  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_QKV, SB>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_SWIGLU, NPART, SB>,
+  (void)hipFuncSetAttribute((const void*)gemm_f16_kernel<BM, BN, WGM, WGN, EPI_SWIGLU, SB>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
@@ -555,13 +554,10 @@ static void gemm_init_attributes() {
   static bool done = false;
   if (done) return;
   done = true;
-  gemm_set_lds_limit<256, 256, 2, 4, 1, true>();
+  gemm_set_lds_limit<256, 256, 2, 4, true>();
   gemm_set_lds_limit<128, 128, 2, 2>();
 }
 
-// Tile choice from a sweep of the Llama-3-8B projection shapes at M = 512, 2048
-// and 8192 on MI355X: the 8-wave 256 x 256 tile when it still yields at least 192
-// tiles, then 128 x 128 with at least 256 tiles (one per CU), else 64 x 64.
 // Split-K second pass: out = epilogue(sum over the splits of part[s][m][n]), summed in split
 // order.  One thread per 4 consecutive columns (N % 4 == 0), so RoPE partners (2j, 2j+1)
 // and SwiGLU gate/up pairs (2c, 2c+1) are in the same thread.
@@ -740,7 +736,7 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
   // The q|k|v epilogue (RoPE table reads, cache addressing) does not fit the register-staged
   // 256 x 256 tile's registers (it spills), so that projection stays on 128 x 128 tiles.
   if (M > 128 && ep.kind != EPI_QKV && tiles(256, 256) >= 192)
-    gemm_dispatch<256, 256, 2, 4, 1, true>(a, w, M, N, K, ep, s);
+    gemm_dispatch<256, 256, 2, 4, true>(a, w, M, N, K, ep, s);
   else if (M > 64 && tiles(128, 128) >= 256)
     gemm_dispatch<128, 128, 2, 2>(a, w, M, N, K, ep, s);
   else
