@@ -877,12 +877,11 @@ bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads) {
 template <int HPW>
 static void attn_prefill_launch(dim3 grid, hipStream_t s, const f16_t* q, const f16_t* k, const f16_t* v, int slot,
                                 int pos0, int n_tokens, int H, int G, int max_seq, f16_t* out) {
-  static bool attr = false;  // the double-buffered tiles exceed the default 64 KiB dynamic LDS limit
-  if (!attr) {
-    attr = true;
-    (void)hipFuncSetAttribute((const void*)attn_prefill_kernel<HPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)PF_LDS_BYTES);
-  }
+  // The double-buffered tiles exceed the default 64 KiB dynamic LDS limit, raised once (a
+  // function-local static is initialised exactly once even with concurrent callers).
+  static const hipError_t attr = hipFuncSetAttribute((const void*)attn_prefill_kernel<HPW>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)PF_LDS_BYTES);
+  (void)attr;
   launch_k(attn_prefill_kernel<HPW>, grid, 256, PF_LDS_BYTES, s, q, k, v, slot, pos0, n_tokens, H, G, max_seq, out);
 }
 

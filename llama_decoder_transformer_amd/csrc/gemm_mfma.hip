@@ -472,9 +472,9 @@ static int gemm_dma_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K
   const dim3 grid(tm * tn, (nkb + kb_per - 1) / kb_per);
   const int nt = 64 * WGM * WGN;
   constexpr size_t lds = gemm_dma_lds_bytes<BM, BN, NS>();
-  static bool attr = false;  // above 64 KiB the per-kernel dynamic LDS limit must be raised once
-  if (!attr) {
-    attr = true;
+  // Above 64 KiB the per-kernel dynamic LDS limit must be raised, once (a function-local static
+  // is initialised exactly once even with concurrent callers).
+  static const bool attr = [] {
     (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_STORE_F32, SCHED>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_RESID, SCHED>,
@@ -483,7 +483,9 @@ static int gemm_dma_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipFuncSetAttribute((const void*)gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_SWIGLU, SCHED>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  }
+    return true;
+  }();
+  (void)attr;
   switch (ep.kind) {
     case EPI_STORE_F32:
       launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_STORE_F32, SCHED>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
@@ -551,11 +553,12 @@ static void gemm_set_lds_limit() {
 
 // Tiles above 64 KiB of LDS need the per-kernel dynamic limit raised once.
 static void gemm_init_attributes() {
-  static bool done = false;
-  if (done) return;
-  done = true;
-  gemm_set_lds_limit<256, 256, 2, 4, true>();
-  gemm_set_lds_limit<128, 128, 2, 2>();
+  static const bool done = [] {
+    gemm_set_lds_limit<256, 256, 2, 4, true>();
+    gemm_set_lds_limit<128, 128, 2, 2>();
+    return true;
+  }();
+  (void)done;
 }
 
 // Split-K second pass: out = epilogue(sum over the splits of part[s][m][n]), summed in split
