@@ -398,14 +398,9 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 // or more heads).  Heaviest causal blocks are scheduled first.
 //
 // Per 64-key tile a wave computes S^T = K Q^T (keys as MFMA rows, queries as
-// columns), so each lane's accumulators all belong to one query column: the
-// softmax max needs only two cross-lane steps and the scaled probabilities,
-// packed to fp16, are already the B operand of O^T += V^T P^T.  The k-order of
-// that second product is the permutation {4g..4g+3, 16+4g..16+4g+3} of each
-// 32-key slice that the first product leaves in lane group g.  V stays row-major
-// in LDS; the transposing LDS read (ds_read_b64_tr_b16: lane i of a 16-lane group
-// receives element i%4 of the 4-element reads of lanes i/4, 4+i/4, 8+i/4, 12+i/4)
-// turns two 8-byte reads per lane into exactly that V^T fragment.
+// columns), so each lane's accumulators all belong to one query column and the
+// scaled probabilities, packed to fp16, are already the B operand of
+// O^T += V^T P^T (details at the kernel).
 //
 // K/V tiles are double-buffered in LDS: the next tile's global loads are issued
 // into registers before the current tile's math, stored after it, and a single
@@ -432,49 +427,59 @@ __device__ __forceinline__ uint2 pf_read_tr(const f16_t* lds_elem) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// The products run on v_mfma_f32_32x32x16_f16 (twice the issue rate of 16x16x32 on this GPU:
+// 79 against 88 us at S = 2048, 788 against 876 us at S = 8192).  Per 64-key tile a wave (32
+// queries of one head) computes S^T = K Q^T as 2 key blocks x 8 dimension slices of 16: lane l
+// holds query l % 32 and keys (e % 4) + 8 (e / 4) + 4 (l / 32) of each 32-key block, so a
+// query's 64 scores sit in lanes l and l ^ 32 and the softmax needs one cross-lane step.
+// O^T += V^T P^T takes 16 keys per product: k-step t (block t / 2, half t % 2) uses this lane's
+// own probabilities e = 8 (t % 2) .. +7 as its B operand, i.e. keys {0..3, 8..11} (lanes < 32)
+// and {4..7, 12..15} (lanes >= 32) of the half, and the V^T operand is assembled in that key
+// order from row-major V by two transposing LDS reads (ds_read_b64_tr_b16: lane i of a 16-lane
+// group receives element i % 4 of the reads of lanes i / 4 + 4 j, so lane 4 j + c addresses key j
+// of its 4-key run at columns 4 c .. 4 c + 3).
 template <int HPW>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc,
-                                                           const f16_t* __restrict__ vc, int slot, int pos0, int S,
-                                                           int H, int G, int max_seq, f16_t* __restrict__ out) {
-  constexpr int QSUB = 4 / HPW;  // 32-query sub-blocks per workgroup
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, const f16_t* __restrict__ vc,
+                      int slot, int pos0, int S, int H, int G, int max_seq, f16_t* __restrict__ out) {
+  typedef float f32x16_t __attribute__((ext_vector_type(16)));
+  constexpr int QSUB = 4 / HPW;
   constexpr int QB = 32 * QSUB;
   extern __shared__ __attribute__((aligned(16))) f16_t pf_smem[];
-  f16_t* const Ks0 = pf_smem;                 // [2][PF_KT][PF_KLD]
-  f16_t* const Vs0 = pf_smem + 2 * PF_KTILE;  // [2][PF_KT][PF_VLD]
+  f16_t* const Ks0 = pf_smem;
+  f16_t* const Vs0 = pf_smem + 2 * PF_KTILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;
+  const int l32 = lane & 31, lh = lane >> 5;
   const int hpg = H / G;
   const int nhb = hpg / HPW;
   const int qblk = gridDim.x - 1 - blockIdx.x;
   const int g = blockIdx.y / nhb;
   const int head = g * hpg + (blockIdx.y % nhb) * HPW + (wid % HPW);
-  const int qw0 = qblk * QB + 32 * (wid / HPW);  // first query row of this wave
+  const int qw0 = qblk * QB + 32 * (wid / HPW);
   const int wg_last = min(S, qblk * QB + QB) - 1;
-  const int kv_end = pos0 + wg_last + 1;           // keys [0, kv_end) can be seen
+  const int kv_end = pos0 + wg_last + 1;
   const int ld_q = H * PF_D;
   const float scale = LOG2E_F / sqrtf((float)PF_D);
 
-  // Q fragments (B operand): column = query jq*16 + l16, k = 32 s + 8 lg .. +7.
-  f16x8_t qf[2][4];
+  // Q^T fragments (B operand): column = query l32, k = dims 16 s + 8 lh .. +7.
+  f16x8_t qf[8];
+  {
+    const int i = qw0 + l32;
 #pragma unroll
-  for (int jq = 0; jq < 2; ++jq) {
-    const int i = qw0 + jq * 16 + l16;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
+    for (int s8 = 0; s8 < 8; ++s8) {
       u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (i < S) raw = *reinterpret_cast<const u32x4_t*>(q + (size_t)i * ld_q + head * PF_D + s4 * 32 + lg * 8);
-      qf[jq][s4] = __builtin_bit_cast(f16x8_t, raw);
+      if (i < S) raw = *reinterpret_cast<const u32x4_t*>(q + (size_t)i * ld_q + head * PF_D + s8 * 16 + lh * 8);
+      qf[s8] = __builtin_bit_cast(f16x8_t, raw);
     }
   }
 
-  f32x4_t o[8][2];
+  f32x16_t o[4];  // O^T blocks of 32 dimensions
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int jq = 0; jq < 2; ++jq) o[mb][jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // mrow: running max in the scaled log2 domain; lrow: this lane's part of the running sum.
-  float mrow[2] = {-1e30f, -1e30f}, lrow[2] = {0.f, 0.f};
+    for (int e = 0; e < 16; ++e) o[mb][e] = 0.f;
+  float mrow = -1e30f, lrow = 0.f;  // this lane's query: running max (log2 domain), partial sum
 
   const size_t base = ((size_t)slot * G + g) * (size_t)max_seq * PF_D;
   const f16_t* kb = kc + base;
@@ -482,8 +487,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int ntiles = (kv_end + PF_KT - 1) / PF_KT;
   const int wave_first_pos = pos0 + qw0;
   const int wave_last_pos = wave_first_pos + 31;
+  const int qpos = wave_first_pos + l32;
 
-  // Tile copy: 16 lanes per key row, 4 rows of K and of V per thread; keys past kv_end read as zero.
   u32x4_t kr[4], vr[4];
   auto fetch = [&](int k0) {
 #pragma unroll
@@ -512,6 +517,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   stash(0);
   __syncthreads();
 
+  // V^T read address of this lane: key row 4 lh + (l % 16) / 4 of a 16-key half, columns
+  // 16 ((l / 16) % 2) + 4 (l % 4) of a 32-dimension block.
+  const int v_row = 4 * lh + ((lane & 15) >> 2);
+  const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * PF_KT;
     const bool more = t + 1 < ntiles;
@@ -519,103 +529,72 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const f16_t* Ks = Ks0 + (t & 1) * PF_KTILE;
     const f16_t* Vs = Vs0 + (t & 1) * PF_VTILE;
 
-    if (k0 <= wave_last_pos) {  // otherwise every key of this tile is in this wave's future
-      // S^T = K Q^T : st[kb][jq][r] = score(key k0 + 16 kb + 4 lg + r, query jq*16 + l16)
-      f32x4_t st[4][2];
+    if (k0 <= wave_last_pos) {
+      // st[kb][e] = score(key k0 + 32 kb + (e % 4) + 8 (e / 4) + 4 lh, query l32)
+      f32x16_t st[2];
 #pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int jq = 0; jq < 2; ++jq) st[kb4][jq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 16; ++e) st[kb2][e] = 0.f;
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
+      for (int s8 = 0; s8 < 8; ++s8) {
 #pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4) {
-          const f16x8_t kf = *reinterpret_cast<const f16x8_t*>(&Ks[(kb4 * 16 + l16) * PF_KLD + s4 * 32 + lg * 8]);
-#pragma unroll
-          for (int jq = 0; jq < 2; ++jq)
-            st[kb4][jq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[jq][s4], st[kb4][jq], 0, 0, 0);
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const f16x8_t kf = *reinterpret_cast<const f16x8_t*>(&Ks[(kb2 * 32 + l32) * PF_KLD + s8 * 16 + lh * 8]);
+          st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s8], st[kb2], 0, 0, 0);
         }
       }
-
-      // Causal mask, only on tiles that reach past this wave's first query.
       if (k0 + PF_KT - 1 > wave_first_pos) {
 #pragma unroll
-        for (int jq = 0; jq < 2; ++jq) {
-          const int qpos = wave_first_pos + jq * 16 + l16;
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-          for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (k0 + kb4 * 16 + lg * 4 + r > qpos) st[kb4][jq][r] = -INFINITY;
-        }
+          for (int e = 0; e < 16; ++e)
+            if (k0 + kb2 * 32 + (e & 3) + 8 * (e >> 2) + 4 * lh > qpos) st[kb2][e] = -INFINITY;
       }
-
-      // Online softmax per query column (raw scores; scale > 0 keeps the max).
-      float tmax[2];
+      float m = st[0][0];
 #pragma unroll
-      for (int jq = 0; jq < 2; ++jq) {
-        float m = st[0][jq][0];
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4)
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, st[kb2][e]);
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const float tmax = m * scale;
+      if (__any(tmax > mrow + PF_RESCALE_LOG2)) {
+        const float mn = fmaxf(mrow, tmax);
+        const float alpha = exp2f(mrow - mn);
+        mrow = mn;
+        lrow *= alpha;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) m = fmaxf(m, st[kb4][jq][r]);
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        tmax[jq] = m * scale;
+        for (int mb = 0; mb < 4; ++mb) o[mb] *= alpha;
       }
-      const bool raise = tmax[0] > mrow[0] + PF_RESCALE_LOG2 || tmax[1] > mrow[1] + PF_RESCALE_LOG2;
-      if (__any(raise)) {
+      const float mneg = -mrow;
+      // P^T operands: k-step t4 = (block t4 / 2, half t4 % 2) holds scores e = 8 (t4 % 2) .. +7.
+      f16x8_t pf[4];
 #pragma unroll
-        for (int jq = 0; jq < 2; ++jq) {
-          const float mn = fmaxf(mrow[jq], tmax[jq]);
-          const float alpha = exp2f(mrow[jq] - mn);
-          mrow[jq] = mn;
-          lrow[jq] *= alpha;
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-          for (int mb = 0; mb < 8; ++mb) o[mb][jq] *= alpha;
-        }
-      }
-      f16x8_t pf[2][2];  // [jq][k-step of 32 keys]
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t pk[4];
 #pragma unroll
-      for (int jq = 0; jq < 2; ++jq) {
-        const float mneg = -mrow[jq];
-        float psum = 0.f;
-        uint32_t packed[2][4];
-#pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4) {
-          float p[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(fmaf(st[kb4][jq][r], scale, mneg));
-            psum += p[r];
+          for (int i = 0; i < 4; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kb2][8 * hh + 2 * i], scale, mneg));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kb2][8 * hh + 2 * i + 1], scale, mneg));
+            lrow += p0 + p1;
+            pk[i] = pack_f16x2(p0, p1);
           }
-          // k-step kb4/2 holds blocks 2t (elements 0..3) and 2t+1 (elements 4..7).
-          const int ks = kb4 >> 1, half = (kb4 & 1) * 2;
-          packed[ks][half] = pack_f16x2(p[0], p[1]);
-          packed[ks][half + 1] = pack_f16x2(p[2], p[3]);
-        }
-        lrow[jq] += psum;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          u32x4_t u = {packed[ks][0], packed[ks][1], packed[ks][2], packed[ks][3]};
-          pf[jq][ks] = __builtin_bit_cast(f16x8_t, u);
+          const u32x4_t u = {pk[0], pk[1], pk[2], pk[3]};
+          pf[2 * kb2 + hh] = __builtin_bit_cast(f16x8_t, u);
         }
       }
-
-      // O^T += V^T P^T.  A operand row d = 16 mb + l16, k = keys {4 lg + j, 16 + 4 lg + j} of the 32-key step:
-      // this lane's transposing reads address key row 32 ks + 4 lg + l16/4 (and +16), columns 16 mb + 4 (l16%4)..+3.
-      const f16_t* vlane = Vs + (4 * lg + (l16 >> 2)) * PF_VLD + 4 * (l16 & 3);
+      // O^T += V^T P^T
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const f16_t* vrow = Vs + (16 * t4 + v_row) * PF_VLD + v_col;
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-          const uint2 lo = pf_read_tr(vlane + (32 * ks) * PF_VLD + 16 * mb);
-          const uint2 hi = pf_read_tr(vlane + (32 * ks + 16) * PF_VLD + 16 * mb);
+        for (int mb = 0; mb < 4; ++mb) {
+          const uint2 lo = pf_read_tr(vrow + 32 * mb);
+          const uint2 hi = pf_read_tr(vrow + 8 * PF_VLD + 32 * mb);
           const u32x4_t u = {lo.x, lo.y, hi.x, hi.y};
-          const f16x8_t vf = __builtin_bit_cast(f16x8_t, u);
-#pragma unroll
-          for (int jq = 0; jq < 2; ++jq)
-            o[mb][jq] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[jq][ks], o[mb][jq], 0, 0, 0);
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, u), pf[t4], o[mb], 0, 0, 0);
         }
       }
     }
@@ -624,24 +603,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
   }
 
-  // Normalise and store: lane holds d = 16 mb + 4 lg + r of query jq*16 + l16.
+  // Normalise and store: lane holds dims 32 mb + (e % 4) + 8 (e / 4) + 4 lh of query l32.
+  float L = lrow + __shfl_xor(lrow, 32);
+  const float inv = 1.0f / L;
+  const int i = qw0 + l32;
+  if (i < S) {
+    f16_t* orow = out + (size_t)i * ld_q + head * PF_D;
 #pragma unroll
-  for (int jq = 0; jq < 2; ++jq) {
-    float L = lrow[jq];
-    L += __shfl_xor(L, 16);
-    L += __shfl_xor(L, 32);
-    const float inv = 1.0f / L;
-    const int i = qw0 + jq * 16 + l16;
-    if (i < S) {
-      f16_t* orow = out + (size_t)i * ld_q + head * PF_D;
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
+      for (int e4 = 0; e4 < 4; ++e4) {
         uint2 w;
-        w.x = pack_f16x2(o[mb][jq][0] * inv, o[mb][jq][1] * inv);
-        w.y = pack_f16x2(o[mb][jq][2] * inv, o[mb][jq][3] * inv);
-        *reinterpret_cast<uint2*>(orow + mb * 16 + lg * 4) = w;
+        w.x = pack_f16x2(o[mb][4 * e4] * inv, o[mb][4 * e4 + 1] * inv);
+        w.y = pack_f16x2(o[mb][4 * e4 + 2] * inv, o[mb][4 * e4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * e4 + 4 * lh) = w;
       }
-    }
   }
 }
 
@@ -876,7 +852,7 @@ bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads) {
 
 template <int HPW>
 static void attn_prefill_launch(dim3 grid, hipStream_t s, const f16_t* q, const f16_t* k, const f16_t* v, int slot,
-                                int pos0, int n_tokens, int H, int G, int max_seq, f16_t* out) {
+                                  int pos0, int n_tokens, int H, int G, int max_seq, f16_t* out) {
   // The double-buffered tiles exceed the default 64 KiB dynamic LDS limit, raised once (a
   // function-local static is initialised exactly once even with concurrent callers).
   static const hipError_t attr = hipFuncSetAttribute((const void*)attn_prefill_kernel<HPW>,
