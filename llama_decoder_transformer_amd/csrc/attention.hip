@@ -413,9 +413,13 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 constexpr int PF_D = 128;
 constexpr int PF_KT = 64;
 constexpr int PF_KLD = PF_D + 8;    // K row stride: 272 bytes (b128 fragment reads: 16 rows hit 64 distinct banks)
-constexpr int PF_VLD = PF_D + 16;   // V row stride: 288 bytes (transposing reads: 8 rows x 32 bytes, distinct banks)
+constexpr int PF_VLD = PF_D + 16;   // decode V tile row stride: 288 bytes (transposing reads of 8 rows x 32 bytes hit distinct banks)
+// Prefill V tile row stride: 320 bytes.  A 32-lane half of a transposing read covers 4 key rows x
+// 64 bytes; rows 64 bytes (16 banks) apart modulo 256 keep them on distinct banks (at 288 bytes
+// a quarter of the LDS cycles were bank conflicts).
 constexpr int PF_KTILE = PF_KT * PF_KLD;  // elements
-constexpr int PF_VTILE = PF_KT * PF_VLD;
+constexpr int PF_VLD2 = PF_D + 32;
+constexpr int PF_VTILE = PF_KT * PF_VLD2;
 constexpr size_t PF_LDS_BYTES = 2 * (size_t)(PF_KTILE + PF_VTILE) * sizeof(f16_t);
 constexpr float PF_RESCALE_LOG2 = 8.0f;
 
@@ -509,7 +513,7 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + i * 256, key = idx >> 4, c = idx & 15;
       *reinterpret_cast<u32x4_t*>(&Ks[key * PF_KLD + c * 8]) = kr[i];
-      *reinterpret_cast<u32x4_t*>(&Vs[key * PF_VLD + c * 8]) = vr[i];
+      *reinterpret_cast<u32x4_t*>(&Vs[key * PF_VLD2 + c * 8]) = vr[i];
     }
   };
 
@@ -588,11 +592,11 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
       // O^T += V^T P^T
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        const f16_t* vrow = Vs + (16 * t4 + v_row) * PF_VLD + v_col;
+        const f16_t* vrow = Vs + (16 * t4 + v_row) * PF_VLD2 + v_col;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           const uint2 lo = pf_read_tr(vrow + 32 * mb);
-          const uint2 hi = pf_read_tr(vrow + 8 * PF_VLD + 32 * mb);
+          const uint2 hi = pf_read_tr(vrow + 8 * PF_VLD2 + 32 * mb);
           const u32x4_t u = {lo.x, lo.y, hi.x, hi.y};
           o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, u), pf[t4], o[mb], 0, 0, 0);
         }
