@@ -7,8 +7,9 @@
 //
 // Two kernels share the tiling, fragment layout and epilogues: gemm_dma_kernel (the LDS-DMA
 // pipeline further below) serves every K % 32 == 0 shape but a batch's LM head, and the
-// register-staged gemm_f16_kernel described here serves the rest.  launch_gemm_f16 at the
-// end of the file picks tiles and K splits per shape.
+// register-staged gemm_f16_kernel described here serves the rest.  A third, gemm_stream_kernel,
+// takes batches of 9 to 64 rows, which stream the weights.  launch_gemm_f16 at the end of the
+// file picks the kernel, tiles and K splits per shape.
 //
 // Tiling: BM x BN output tile per 256-thread workgroup (4 waves as 2 x 2, each
 // owning a BM/2 x BN/2 sub-tile), BK = 64 per stage, v_mfma_f32_16x16x32_f16 on
@@ -561,9 +562,26 @@ static void gemm_init_attributes() {
   (void)done;
 }
 
+// The epilogue of four consecutive columns n .. n+3 of row m (N % 4 == 0 on the paths that use
+// it), so RoPE partners (2j, 2j+1) and SwiGLU gate/up pairs (2c, 2c+1) are together.
+// STORE_F32 writes to `out` (a split's slice of the partial sums, or the output).
+template <int EPI>
+__device__ __forceinline__ void epi_apply4(const EpiParams& ep, float* out, int m, int n, const float (&a)[4]) {
+  if (EPI == EPI_QKV && (ep.head_dim & 3) == 0) {
+    qkv_store4(ep, m, n, a);
+    return;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (EPI == EPI_STORE_F32) out[(size_t)m * ep.ld + n + c] = a[c];
+    else if (EPI == EPI_RESID) ep.out_f32[(size_t)m * ep.ld + n + c] += a[c];
+    else if (EPI == EPI_QKV) epi_qkv<f16_t>(ep, m, n + c, a[c], a[c ^ 1]);
+    else if (EPI == EPI_SWIGLU && (c & 1) == 0) epi_swiglu<f16_t>(ep, m, (n + c) >> 1, a[c], a[c + 1]);
+  }
+}
+
 // Split-K second pass: out = epilogue(sum over the splits of part[s][m][n]), summed in split
-// order.  One thread per 4 consecutive columns (N % 4 == 0), so RoPE partners (2j, 2j+1)
-// and SwiGLU gate/up pairs (2c, 2c+1) are in the same thread.
+// order.  One thread per 4 consecutive columns (N % 4 == 0).
 template <int EPI>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
                                                             EpiParams ep) {
@@ -578,16 +596,213 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
   }
   const float a[4] = {v.x, v.y, v.z, v.w};
-  if (EPI == EPI_QKV && (ep.head_dim & 3) == 0) {
-    qkv_store4(ep, m, n, a);
-    return;
-  }
+  epi_apply4<EPI>(ep, ep.out_f32, m, n, a);
+}
+
+// Weight-streaming GEMM for batches of at most 64 rows (batched decode).  Such a projection is
+// bound by the weight stream, and on this GPU one CU streams at most about 22 GB/s from HBM
+// (measured: 224 workgroups of 128 weight rows, one per CU, reach 4.6 TB/s with or without
+// deeper pipelines; 448 workgroups of 64 rows over all 256 CUs reach 5.6).  So the grid is
+// sized to give every CU one equal share: an N tile of 16 * FN weight rows over one K slice,
+// FN and the slice count chosen per shape (stream_plan), e.g. 256 tiles of 112 rows for the
+// 28672-row gate-up projection.  Any FN works because the 4 waves split each stage's K instead
+// of its columns:
+//  - a stage holds BK = 128 k of the 64 activation rows and the BN weight rows, as 256-byte
+//    row pieces (whole 128-byte lines) brought in by LDS DMA, 16-byte chunk c of row r at
+//    position c ^ (r % 16) (fragment reads of 8 consecutive rows hit distinct banks);
+//  - wave w multiplies k-quarter w of every stage into its own 64 x BN accumulators;
+//  - at the end the four partial tiles meet in LDS, are summed in wave order (deterministic)
+//    and go through the epilogue 4 columns per thread: the output itself when K is not split,
+//    else this slice's partial sums for splitk_reduce_kernel.
+constexpr int ST_BK = 128;
+
+template <int FN, int NS>
+static constexpr size_t stream_lds_bytes() {
+  return std::max((size_t)NS * (64 + 16 * FN) * ST_BK * sizeof(f16_t), (size_t)4 * 64 * 16 * FN * sizeof(float));
+}
+
+template <int FN, int NS, int EPI>
+__global__ void __launch_bounds__(256) gemm_stream_kernel(const f16_t* __restrict__ A, const f16_t* __restrict__ W,
+                                                          int M, int N, int K, EpiParams ep, int kb_per) {
+  constexpr int BM = 64, BN = 16 * FN, ROWS = BM + BN;
+  constexpr int STAGE = ROWS * ST_BK;  // f16 elements per stage
+  constexpr int NI = ROWS / 4;         // DMA instructions per stage: 4 rows x 256 bytes each
+  constexpr int PW = NI / 4;           // ... per wave
+  static_assert(NI % 4 == 0, "DMA instructions do not split evenly over the waves");
+  static_assert(NS >= 3 && NS <= 4 && (NS - 2) * PW < 64, "stages");
+
+  extern __shared__ __attribute__((aligned(16))) f16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int tn = blockIdx.x * BN;
+  const int kb0 = blockIdx.y * kb_per;  // first stage (of ST_BK k) of this slice
+  const int nk = min(kb_per, K / ST_BK - kb0);
+
+  // DMA: instruction j of a stage covers tile rows 4j .. 4j+3 (activation rows first); lane l
+  // lands at row 4j + l/16, physical chunk l % 16, and so loads logical chunk (l % 16) ^ (row % 16).
+  const f16_t* src[PW];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    if (EPI == EPI_STORE_F32) ep.out_f32[(size_t)m * ep.ld + n + c] = a[c];
-    else if (EPI == EPI_RESID) ep.out_f32[(size_t)m * ep.ld + n + c] += a[c];
-    else if (EPI == EPI_QKV) epi_qkv<f16_t>(ep, m, n + c, a[c], a[c ^ 1]);
-    else if ((c & 1) == 0) epi_swiglu<f16_t>(ep, m, (n + c) >> 1, a[c], a[c + 1]);
+  for (int i = 0; i < PW; ++i) {
+    const int j = wid * PW + i;
+    const int r = 4 * j + (lane >> 4);
+    const int col = ((lane & 15) ^ (r & 15)) * 8 + kb0 * ST_BK;
+    src[i] = r < BM ? A + (size_t)min(r, M - 1) * K + col : W + (size_t)min(tn + r - BM, N - 1) * K + col;
+  }
+  auto issue = [&](int buf, int kt) {
+    f16_t* base = smem + buf * STAGE + wid * PW * 4 * ST_BK;
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src[i] + kt * ST_BK),
+                                       (void __attribute__((address_space(3)))*)(base + i * 4 * ST_BK), 16, 0, 0);
+  };
+
+  f32x4_t acc[4][FN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st, st);
+  // Logical chunk of this lane's fragments: k-quarter wid of the stage, 8 k per lane group.
+  const int fc = ((4 * wid + lg) ^ l16) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt is in LDS once at most min(NS - 2, nk - 1 - kt) later stages are outstanding.
+    const int later = min(NS - 2, nk - 1 - kt);
+    if (later >= 2) wait_vmcnt<2 * PW>();
+    else if (later == 1) wait_vmcnt<PW>();
+    else wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // The buffer of stage kt - 1 is free: every wave finished reading it before this barrier.
+    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
+    const f16_t* As = smem + (kt % NS) * STAGE;
+    const f16_t* Ws = As + BM * ST_BK;
+    f16x8_t af[4], bw[FN];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const f16x8_t*>(As + (i * 16 + l16) * ST_BK + fc);
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) bw[jn] = *reinterpret_cast<const f16x8_t*>(Ws + (jn * 16 + l16) * ST_BK + fc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < FN; ++jn)
+        acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bw[jn], acc[i][jn], 0, 0, 0);
+  }
+
+  // The four waves' partial tiles meet in LDS ([wave][row][col] floats over the stage buffers).
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(wid * BM + i * 16 + lg * 4 + r) * BN + jn * 16 + l16] = acc[i][jn][r];
+  __syncthreads();
+  float* out = EPI == EPI_STORE_F32 ? ep.out_f32 + (size_t)blockIdx.y * M * ep.ld : ep.out_f32;
+  for (int g = tid; g < BM * BN / 4; g += 256) {
+    const int m = g / (BN / 4), c4 = (g % (BN / 4)) * 4;
+    if (m >= M || tn + c4 >= N) continue;
+    float4 v = *reinterpret_cast<const float4*>(red + m * BN + c4);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float4 u = *reinterpret_cast<const float4*>(red + (w * BM + m) * BN + c4);
+      v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+    }
+    const float a[4] = {v.x, v.y, v.z, v.w};
+    epi_apply4<EPI>(ep, out, m, tn + c4, a);
+  }
+}
+
+// Launch over N / (16 FN) tiles and `splits` K slices (whole stages of ST_BK each); returns the
+// slice count.  Requires M <= 64, K % ST_BK == 0 and N % 4 == 0.
+template <int FN, int NS>
+static int gemm_stream_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep,
+                                hipStream_t s, int splits) {
+  constexpr int BN = 16 * FN;
+  const int nkb = K / ST_BK;
+  const int kb_per = (nkb + splits - 1) / splits;
+  const dim3 grid((N + BN - 1) / BN, (nkb + kb_per - 1) / kb_per);
+  constexpr size_t lds = stream_lds_bytes<FN, NS>();
+  static const bool attr = [] {
+    (void)hipFuncSetAttribute((const void*)gemm_stream_kernel<FN, NS, EPI_STORE_F32>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)gemm_stream_kernel<FN, NS, EPI_RESID>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)gemm_stream_kernel<FN, NS, EPI_QKV>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)gemm_stream_kernel<FN, NS, EPI_SWIGLU>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    return true;
+  }();
+  (void)attr;
+  switch (ep.kind) {
+    case EPI_STORE_F32:
+      launch_k(gemm_stream_kernel<FN, NS, EPI_STORE_F32>, grid, 256, lds, s, A, W, M, N, K, ep, kb_per);
+      break;
+    case EPI_RESID:
+      launch_k(gemm_stream_kernel<FN, NS, EPI_RESID>, grid, 256, lds, s, A, W, M, N, K, ep, kb_per);
+      break;
+    case EPI_QKV:
+      launch_k(gemm_stream_kernel<FN, NS, EPI_QKV>, grid, 256, lds, s, A, W, M, N, K, ep, kb_per);
+      break;
+    case EPI_SWIGLU:
+      launch_k(gemm_stream_kernel<FN, NS, EPI_SWIGLU>, grid, 256, lds, s, A, W, M, N, K, ep, kb_per);
+      break;
+  }
+  return (int)grid.y;
+}
+
+// Plan of the weight-streaming kernel for 8 < M <= 64: FN (tile of 16 FN weight rows) and the
+// K slice count S, over the tiles that divide N.  The rule, from a sweep of the Llama-3-8B
+// projections at 64 and 40 rows on MI355X (weights rotated over copies so HBM is measured):
+// the most workgroups up to 256 (one per CU; fewer leave CUs idle, more queue behind them),
+// then tiles of at least 48 rows (narrower ones re-read the activations for too few weights:
+// down on 32-row tiles 3.5 TB/s against 4.2 on 64), then the fewest slices (each slice adds
+// a pass over fp32 partial sums).  E.g. q|k|v 3 x 2 slices 3.9 TB/s (was 2.9), wo 4 x 4
+// slices 2.9 (2.5), gate-up 7 unsplit 4.6 (4.3), down 4 x 4 slices 4.2 (3.8).  Returns false
+// when no plan gives more than 128 workgroups or the shape does not fit (K % 128, N % 4).
+struct StreamPlan {
+  int fn;
+  int splits;
+};
+
+static bool stream_plan(int M, int N, int K, StreamPlan& p) {
+  if (M <= 8 || M > 64 || K % ST_BK != 0 || N % 4 != 0) return false;
+  static const int fns[] = {2, 3, 4, 6, 7, 8};
+  const int nkb = K / ST_BK;
+  bool found = false;
+  long best[3] = {0, 0, 0};  // (workgroups, tile of >= 48 rows, -slices), compared in order
+  for (int sp = 1; sp <= 8; sp *= 2) {
+    if (nkb / sp < 4) break;
+    for (int fn : fns) {
+      if (N % (16 * fn) != 0) continue;
+      const long wg = (long)(N / (16 * fn)) * sp;
+      if (wg > 256 || wg <= 128) continue;
+      const long key[3] = {wg, fn >= 3, -sp};
+      if (!found || std::lexicographical_compare(best, best + 3, key, key + 3)) {
+        std::copy(key, key + 3, best);
+        p = {fn, sp};
+        found = true;
+      }
+    }
+  }
+  return found;
+}
+
+// Launch a stream plan; returns the number of K slices (partial sums to reduce when > 1).
+static int gemm_stream_run(const StreamPlan& p, const f16_t* A, const f16_t* W, int M, int N, int K,
+                           const EpiParams& ep, hipStream_t s) {
+  switch (p.fn) {
+    case 2: return gemm_stream_dispatch<2, 3>(A, W, M, N, K, ep, s, p.splits);
+    case 3: return gemm_stream_dispatch<3, 3>(A, W, M, N, K, ep, s, p.splits);
+    case 4: return gemm_stream_dispatch<4, 3>(A, W, M, N, K, ep, s, p.splits);
+    case 6: return gemm_stream_dispatch<6, 3>(A, W, M, N, K, ep, s, p.splits);
+    case 7: return gemm_stream_dispatch<7, 3>(A, W, M, N, K, ep, s, p.splits);
+    default: return gemm_stream_dispatch<8, 3>(A, W, M, N, K, ep, s, p.splits);
   }
 }
 
@@ -650,11 +865,14 @@ size_t gemm_splitk_floats(int M, int N, int K) {
     if (big_tile_plan(M, N, K, qkv, bp) && bp.splits > 1) need = std::max(need, (size_t)bp.splits * M * N);
   const int sp = gemm_splitk_count(M, N, K);
   if (sp > 1) need = std::max(need, (size_t)sp * M * N);
+  StreamPlan st;
+  if (stream_plan(M, N, K, st) && st.splits > 1) need = std::max(need, (size_t)st.splits * M * N);
   return need;
 }
 
-// Tile choice from sweeps of the Llama-3-8B projection shapes at M = 256 .. 8192 on MI355X.
-// Shapes with K % 32 == 0 use the LDS-DMA kernel: M <= 128 split over K on 64 x 64 tiles
+// Tile choice from sweeps of the Llama-3-8B projection shapes at M = 16 .. 8192 on MI355X.
+// 8 < M <= 64 with K % 128 == 0 streams the weights through gemm_stream_kernel (stream_plan).
+// Other shapes with K % 32 == 0 use the LDS-DMA kernel: M <= 128 split over K on 64 x 64 tiles
 // (gemm_splitk_count); larger M as big_tile_plan says (256 x 256 or 256 x 128 tiles, split
 // over K when they are too few), then 128 x 128 with at least 192 tiles, else 64 x 64.  Other
 // K use the register-staged kernel.
@@ -686,6 +904,21 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
       const int ns = bp.tile == 0 ? gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, pe, s, bp.splits)
                                   : gemm_dma_dispatch<256, 128, 4, 2, 4, true>(a, w, M, N, K, pe, s, bp.splits);
       reduce(ns);
+      return;
+    }
+  }
+  {
+    StreamPlan st;
+    if (stream_plan(M, N, K, st) && (st.splits == 1 || (splitk_ws && (size_t)st.splits * M * N <= splitk_ws_floats))) {
+      if (st.splits == 1) {
+        gemm_stream_run(st, a, w, M, N, K, ep, s);
+      } else {
+        EpiParams pe = ep;
+        pe.kind = EPI_STORE_F32;
+        pe.out_f32 = splitk_ws;
+        pe.ld = N;
+        reduce(gemm_stream_run(st, a, w, M, N, K, pe, s));
+      }
       return;
     }
   }
