@@ -599,6 +599,57 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
   epi_apply4<EPI>(ep, ep.out_f32, m, n, a);
 }
 
+// Split-K reduction of a residual projection fused with the RMSNorm that consumes its result:
+// x[m] += (sum over the splits of part[s][m], in split order), then
+// a[m] = fp16(x[m] / sqrt(mean(x[m]^2) + eps) * w), fp32 statistics summed in a fixed order.
+// One 1024-thread workgroup per row, V4 float4 of the row per thread (N % 4 == 0,
+// N <= 4096 V4), so a row's loads all go out at once.
+template <int V4>
+__global__ void __launch_bounds__(1024) splitk_resid_norm_kernel(const float* __restrict__ part, int splits, int M,
+                                                                 int N, float* __restrict__ x, int ldx,
+                                                                 const float* __restrict__ w, float eps,
+                                                                 f16_t* __restrict__ a) {
+  __shared__ float red[16];
+  const int m = blockIdx.x;
+  const size_t slice = (size_t)M * N;
+  float* xr = x + (size_t)m * ldx;
+  f32x4_t v[V4];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < V4; ++j) {
+    const int i = (threadIdx.x + 1024 * j) * 4;
+    if (i < N) {
+      float4 p = *reinterpret_cast<const float4*>(part + (size_t)m * N + i);
+      for (int sp = 1; sp < splits; ++sp) {
+        const float4 q = *reinterpret_cast<const float4*>(part + (size_t)sp * slice + (size_t)m * N + i);
+        p.x += q.x; p.y += q.y; p.z += q.z; p.w += q.w;
+      }
+      const float4 xo = *reinterpret_cast<const float4*>(xr + i);
+      v[j] = f32x4_t{xo.x + p.x, xo.y + p.y, xo.z + p.z, xo.w + p.w};
+      *reinterpret_cast<float4*>(xr + i) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+      ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+    }
+  }
+  ss = wave_sum(ss);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) red[wid] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tot += red[i];
+  const float inv = 1.0f / sqrtf(tot / (float)N + eps);
+  f16_t* ar = a + (size_t)m * N;
+#pragma unroll
+  for (int j = 0; j < V4; ++j) {
+    const int i = (threadIdx.x + 1024 * j) * 4;
+    if (i < N) {
+      const f32x4_t g = *reinterpret_cast<const f32x4_t*>(w + i);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ar[i + k] = from_f32<f16_t>(v[j][k] * inv * g[k]);
+    }
+  }
+}
+
 // Weight-streaming GEMM for batches of at most 64 rows (batched decode).  Such a projection is
 // bound by the weight stream, and on this GPU one CU streams at most about 22 GB/s from HBM
 // (measured: 224 workgroups of 128 weight rows, one per CU, reach 4.6 TB/s with or without
@@ -977,6 +1028,30 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
     gemm_dispatch<128, 128, 2, 2>(a, w, M, N, K, ep, s);
   else
     gemm_dispatch<64, 64, 2, 2>(a, w, M, N, K, ep, s);
+}
+
+
+// x += A W^T (a residual projection, ep.kind == EPI_RESID) followed by a = rmsnorm(x) * norm_w in
+// fp16, for shapes the weight-streaming plan splits over K: the reduction pass of the partial
+// sums also applies the RMSNorm, which saves a launch.  Returns false, enqueueing nothing, for
+// other shapes; the caller then runs the projection and the RMSNorm separately.
+bool launch_gemm_f16_resid_norm(const void* A, const void* W, int M, int N, int K, const EpiParams& ep,
+                                const float* norm_w, float eps, void* a_out, float* splitk_ws,
+                                size_t splitk_ws_floats, hipStream_t s) {
+  if (ep.kind != EPI_RESID || M <= 0 || N % 4 != 0 || N > 8192 || ep.ld != N || !splitk_ws) return false;
+  StreamPlan st;
+  if (!stream_plan(M, N, K, st) || st.splits < 2 || (size_t)st.splits * M * N > splitk_ws_floats) return false;
+  EpiParams pe = ep;
+  pe.kind = EPI_STORE_F32;
+  pe.out_f32 = splitk_ws;
+  pe.ld = N;
+  const int ns = gemm_stream_run(st, (const f16_t*)A, (const f16_t*)W, M, N, K, pe, s);
+  f16_t* a = (f16_t*)a_out;
+  if (N <= 4096)
+    launch_k(splitk_resid_norm_kernel<1>, M, 1024, 0, s, splitk_ws, ns, M, N, ep.out_f32, ep.ld, norm_w, eps, a);
+  else
+    launch_k(splitk_resid_norm_kernel<2>, M, 1024, 0, s, splitk_ws, ns, M, N, ep.out_f32, ep.ld, norm_w, eps, a);
+  return true;
 }
 
 }  // namespace llm

@@ -85,6 +85,12 @@ int gemm_splitk_count(int M, int N, int K);
 size_t gemm_splitk_floats(int M, int N, int K);
 void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const EpiParams& ep, float* splitk_ws,
                      size_t splitk_ws_floats, hipStream_t s);
+// x += A W^T (ep.kind == EPI_RESID, ep.out_f32 = x with ld N) and then a = fp16(rmsnorm(x) * norm_w)
+// in the split-K reduction pass, when the weight-streaming plan splits this shape over K.
+// Returns false and enqueues nothing otherwise.
+bool launch_gemm_f16_resid_norm(const void* A, const void* W, int M, int N, int K, const EpiParams& ep,
+                                const float* norm_w, float eps, void* a_out, float* splitk_ws,
+                                size_t splitk_ws_floats, hipStream_t s);
 // Vector GEMV for small M.  With norm_w == nullptr, A has the activation dtype; otherwise A
 // is the fp32 residual stream and the RMSNorm (weight norm_w, eps) is fused into the pass.
 void launch_gemv(int dtype, const void* A, const void* W, const float* norm_w, float eps, int M, int N, int K,

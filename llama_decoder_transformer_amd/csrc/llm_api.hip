@@ -295,8 +295,13 @@ struct SeqSpan {
   int row0, n, start, slot;
 };
 
-void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_slot, int pos0, int slot0,
-               bool prefill, hipStream_t s, const std::vector<SeqSpan>* seqs = nullptr) {
+// a_ready: m->a already holds rmsnorm(x) with this layer's attention norm (left there by the
+// previous layer's down projection).  next_norm: the next layer's attention norm, or null.
+// Returns whether m->a now holds rmsnorm(x) with next_norm.  The two RMSNorms ahead of MFMA
+// projections ride in the split-K reduction of the wo / down projection when that is split.
+bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_slot, int pos0, int slot0,
+               bool prefill, hipStream_t s, const std::vector<SeqSpan>* seqs = nullptr, bool a_ready = false,
+               const float* next_norm = nullptr) {
   const llm_config& c = m->cfg;
   const LayerPtrs& L = m->layers[l];
   const int H = c.n_heads, G = c.n_kv_heads, hd = m->hd, dim = c.dim, F = c.ffn_hidden_dim;
@@ -313,7 +318,10 @@ void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   e.slot0 = slot0;
   {
     Timed t(m, LLM_K_QKV, s);
-    project(m, m->x, L.wqkv, M, (H + 2 * G) * hd, dim, e, s, L.attn_norm);
+    if (a_ready)
+      launch_gemm_f16(m->a, L.wqkv, M, (H + 2 * G) * hd, dim, e, m->splitk, m->splitk_floats, s);
+    else
+      project(m, m->x, L.wqkv, M, (H + 2 * G) * hd, dim, e, s, L.attn_norm);
   }
 
   {
@@ -334,9 +342,13 @@ void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   r.kind = EPI_RESID;
   r.out_f32 = m->x;
   r.ld = dim;
+  bool ffn_ready = false;
   {
     Timed t(m, LLM_K_WO, s);
-    project(m, m->o, L.wo, M, dim, H * hd, r, s);
+    if (use_mfma(m, M))
+      ffn_ready = launch_gemm_f16_resid_norm(m->o, L.wo, M, dim, H * hd, r, L.ffn_norm, c.norm_eps, m->a, m->splitk,
+                                             m->splitk_floats, s);
+    if (!ffn_ready) project(m, m->o, L.wo, M, dim, H * hd, r, s);
   }
 
   EpiParams g = base_epi(m);
@@ -345,13 +357,32 @@ void run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   g.ld = F;
   {
     Timed t(m, LLM_K_GATE_UP, s);
-    project(m, m->x, L.w13, M, 2 * F, dim, g, s, L.ffn_norm);
+    if (ffn_ready)
+      launch_gemm_f16(m->a, L.w13, M, 2 * F, dim, g, m->splitk, m->splitk_floats, s);
+    else
+      project(m, m->x, L.w13, M, 2 * F, dim, g, s, L.ffn_norm);
   }
 
+  bool next_ready = false;
   {
     Timed t(m, LLM_K_DOWN, s);
-    project(m, m->u, L.w2, M, dim, F, r, s);
+    if (next_norm && use_mfma(m, M))
+      next_ready = launch_gemm_f16_resid_norm(m->u, L.w2, M, dim, F, r, next_norm, c.norm_eps, m->a, m->splitk,
+                                              m->splitk_floats, s);
+    if (!next_ready) project(m, m->u, L.w2, M, dim, F, r, s);
   }
+  return next_ready;
+}
+
+// All layers over M rows, each passing its successor the attention-normed activations when its
+// down projection produced them.
+void run_layers(llm_model* m, int M, const int* row_pos, const int* row_slot, int pos0, int slot0, bool prefill,
+                hipStream_t s, const std::vector<SeqSpan>* seqs = nullptr) {
+  const int n = m->cfg.n_layers;
+  bool a_ready = false;
+  for (int l = 0; l < n; ++l)
+    a_ready = run_layer(m, l, M, row_pos, row_slot, pos0, slot0, prefill, s, seqs, a_ready,
+                        l + 1 < n ? m->layers[l + 1].attn_norm : nullptr);
 }
 
 llm_status hip_check(const char* what) {
@@ -378,7 +409,7 @@ void enqueue_decode(llm_model* m, int batch, const int* slots, const int* positi
     Timed t(m, LLM_K_EMBED, s);
     launch_embed(c.dtype, m->emb, tokens, batch, c.dim, c.vocab_size, m->x, m->flags, s);
   }
-  for (int l = 0; l < c.n_layers; ++l) run_layer(m, l, batch, positions, slots, 0, 0, false, s);
+  run_layers(m, batch, positions, slots, 0, 0, false, s);
   lm_head(m, m->x, batch, logits, s);
 }
 
@@ -546,7 +577,7 @@ llm_status llm_prefill(llm_model* m, int32_t slot, const int32_t* tokens_dev, in
     Timed t(m, LLM_K_EMBED, s);
     launch_embed(c.dtype, m->emb, tokens_dev, n_tokens, c.dim, c.vocab_size, m->x, m->flags, s);
   }
-  for (int l = 0; l < c.n_layers; ++l) run_layer(m, l, n_tokens, nullptr, nullptr, start_pos, slot, true, s);
+  run_layers(m, n_tokens, nullptr, nullptr, start_pos, slot, true, s);
   lm_head(m, m->x + (size_t)(n_tokens - 1) * c.dim, 1, logits_dev, s);
   return hip_check("prefill launch");
 }
@@ -599,7 +630,7 @@ llm_status llm_prefill_batch(llm_model* m, int32_t batch, const int32_t* slots_h
     Timed t(m, LLM_K_EMBED, s);
     launch_embed(c.dtype, m->emb, tokens_dev, T, c.dim, c.vocab_size, m->x, m->flags, s);
   }
-  for (int l = 0; l < c.n_layers; ++l) run_layer(m, l, T, row_pos, row_slot, 0, 0, true, s, &seqs);
+  run_layers(m, T, row_pos, row_slot, 0, 0, true, s, &seqs);
   launch_gather_rows(m->x, last_idx, batch, c.dim, m->last, s);
   lm_head(m, m->last, batch, logits_dev, s);
   return hip_check("batched prefill launch");
