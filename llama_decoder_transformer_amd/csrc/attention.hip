@@ -826,10 +826,12 @@ attn_decode_mfma_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ k
 }
 
 // Chunk of the MFMA decode kernel: a multiple of 128 keys (4 waves x 32), halved from 2048
-// until rows x kv-heads x chunks reaches 2048 workgroups.
+// until rows x kv-heads x chunks reaches 4096 workgroups.  With cached lengths spread over
+// U{1024..8192} at 64 rows, 4096 (1024-key chunks) balanced the uneven rows better than 2048
+// (attention 240.5 against 245.3 us per layer on MI355X); one row keeps the 128-key floor.
 static int dec_mfma_chunk(int rows, int n_kv_heads, int max_seq) {
   int ch = 2048;
-  while (ch > 128 && (long)rows * n_kv_heads * ((max_seq + ch - 1) / ch) < 2048) ch >>= 1;
+  while (ch > 128 && (long)rows * n_kv_heads * ((max_seq + ch - 1) / ch) < 4096) ch >>= 1;
   return ch;
 }
 
