@@ -392,9 +392,9 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 // ============================================================== MFMA prefill
 //
 // fp16 operands, fp32 accumulation and softmax, head_dim 128.  Grid (query block, kv-head x head-block).  A workgroup
-// holds 4 waves; each wave owns 32 queries of one query head, and the waves of
+// holds 4 or 8 waves; each wave owns 32 queries of one query head, and the waves of
 // a workgroup share one KV head so a K/V tile of 64 keys is staged in LDS once
-// for all of them (GQA packing: 4 query heads x 32 queries when the group has 4
+// for all of them (GQA packing: 4 query heads x 32 or 64 queries when the group has 4
 // or more heads).  Heaviest causal blocks are scheduled first.
 //
 // Per 64-key tile a wave computes S^T = K Q^T (keys as MFMA rows, queries as
@@ -442,13 +442,15 @@ __device__ __forceinline__ uint2 pf_read_tr(const f16_t* lds_elem) {
 // order from row-major V by two transposing LDS reads (ds_read_b64_tr_b16: lane i of a 16-lane
 // group receives element i % 4 of the reads of lanes i / 4 + 4 j, so lane 4 j + c addresses key j
 // of its 4-key run at columns 4 c .. 4 c + 3).
-template <int HPW>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int HPW, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, const f16_t* __restrict__ vc,
                       int slot, int pos0, int S, int H, int G, int max_seq, f16_t* __restrict__ out) {
   typedef float f32x16_t __attribute__((ext_vector_type(16)));
-  constexpr int QSUB = 4 / HPW;
+  constexpr int QSUB = NW / HPW;  // 32-query sub-blocks per workgroup
   constexpr int QB = 32 * QSUB;
+  constexpr int NT = 64 * NW;     // threads
+  constexpr int NL = 1024 / NT;   // 16-byte loads per thread per K (and V) tile
   extern __shared__ __attribute__((aligned(16))) f16_t pf_smem[];
   f16_t* const Ks0 = pf_smem;
   f16_t* const Vs0 = pf_smem + 2 * PF_KTILE;
@@ -493,11 +495,11 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
   const int wave_last_pos = wave_first_pos + 31;
   const int qpos = wave_first_pos + l32;
 
-  u32x4_t kr[4], vr[4];
+  u32x4_t kr[NL], vr[NL];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + i * 256, key = idx >> 4, c = idx & 15;
+    for (int i = 0; i < NL; ++i) {
+      const int idx = tid + i * NT, key = idx >> 4, c = idx & 15;
       kr[i] = u32x4_t{0u, 0u, 0u, 0u};
       vr[i] = u32x4_t{0u, 0u, 0u, 0u};
       if (k0 + key < kv_end) {
@@ -510,8 +512,8 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
     f16_t* Ks = Ks0 + buf * PF_KTILE;
     f16_t* Vs = Vs0 + buf * PF_VTILE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + i * 256, key = idx >> 4, c = idx & 15;
+    for (int i = 0; i < NL; ++i) {
+      const int idx = tid + i * NT, key = idx >> 4, c = idx & 15;
       *reinterpret_cast<u32x4_t*>(&Ks[key * PF_KLD + c * 8]) = kr[i];
       *reinterpret_cast<u32x4_t*>(&Vs[key * PF_VLD2 + c * 8]) = vr[i];
     }
@@ -856,15 +858,16 @@ bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads) {
   return hpg == 1 || hpg == 2 || hpg % 4 == 0;
 }
 
-template <int HPW>
+template <int HPW, int NW>
 static void attn_prefill_launch(dim3 grid, hipStream_t s, const f16_t* q, const f16_t* k, const f16_t* v, int slot,
                                   int pos0, int n_tokens, int H, int G, int max_seq, f16_t* out) {
   // The double-buffered tiles exceed the default 64 KiB dynamic LDS limit, raised once (a
   // function-local static is initialised exactly once even with concurrent callers).
-  static const hipError_t attr = hipFuncSetAttribute((const void*)attn_prefill_kernel<HPW>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)attn_prefill_kernel<HPW, NW>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)PF_LDS_BYTES);
   (void)attr;
-  launch_k(attn_prefill_kernel<HPW>, grid, 256, PF_LDS_BYTES, s, q, k, v, slot, pos0, n_tokens, H, G, max_seq, out);
+  launch_k(attn_prefill_kernel<HPW, NW>, grid, 64 * NW, PF_LDS_BYTES, s, q, k, v, slot, pos0, n_tokens, H, G, max_seq,
+           out);
 }
 
 void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0, int n_tokens,
@@ -873,18 +876,28 @@ void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache
   (void)head_dim;
   const int hpg = n_heads / n_kv_heads;
   const int hpw = hpg >= 4 ? 4 : hpg;
-  const int qb = 32 * (4 / hpw);
+  // Waves per workgroup: nw / hpw sub-blocks of 32 queries share each K/V tile.  8 waves halve
+  // the tile fills per query but make each causal block heavier; measured on MI355X at the
+  // Llama-3-8B shape: S = 2048 attention 85-88 us with 8 waves against 95 with 4, S = 8192 836
+  // against 739-767.
+  const int nw = n_tokens <= 4096 ? 8 : 4;
+  const int qb = 32 * (nw / hpw);
   dim3 grid((n_tokens + qb - 1) / qb, n_kv_heads * (hpg / hpw));
   const f16_t* qq = (const f16_t*)q;
   const f16_t* kk = (const f16_t*)k_cache;
   const f16_t* vv = (const f16_t*)v_cache;
   f16_t* oo = (f16_t*)out;
-  if (hpw == 4)
-    attn_prefill_launch<4>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
-  else if (hpw == 2)
-    attn_prefill_launch<2>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
-  else
-    attn_prefill_launch<1>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo);
+#define LLM_PF(HPW, NW) attn_prefill_launch<HPW, NW>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo)
+  if (nw == 8) {
+    if (hpw == 4) LLM_PF(4, 8);
+    else if (hpw == 2) LLM_PF(2, 8);
+    else LLM_PF(1, 8);
+  } else {
+    if (hpw == 4) LLM_PF(4, 4);
+    else if (hpw == 2) LLM_PF(2, 4);
+    else LLM_PF(1, 4);
+  }
+#undef LLM_PF
 }
 
 }  // namespace llm
