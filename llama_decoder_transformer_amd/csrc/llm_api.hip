@@ -286,15 +286,15 @@ void project(llm_model* m, const void* A, const void* W, int M, int N, int K, co
   }
 }
 
-// One decoder block on M rows of m->x.  Rows are either a prefill run
-// (row_pos == nullptr: positions pos0.., slot slot0) or decode rows with their
-// own positions and slots.
 // One sequence of a batched prefill: rows [row0, row0 + n) of the workspace, positions start..,
 // cache slot `slot`.
 struct SeqSpan {
   int row0, n, start, slot;
 };
 
+// One decoder block on M rows of m->x.  Rows are either a prefill run
+// (row_pos == nullptr: positions pos0.., slot slot0), a batched prefill (`seqs`), or decode
+// rows with their own positions and slots.
 // a_ready: m->a already holds rmsnorm(x) with this layer's attention norm (left there by the
 // previous layer's down projection).  next_norm: the next layer's attention norm, or null.
 // Returns whether m->a now holds rmsnorm(x) with next_norm.  The two RMSNorms ahead of MFMA
