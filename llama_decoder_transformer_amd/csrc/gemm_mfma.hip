@@ -664,7 +664,8 @@ __global__ void __launch_bounds__(1024) splitk_resid_norm_kernel(const float* __
 //  - wave w multiplies k-quarter w of every stage into its own 64 x BN accumulators;
 //  - at the end the four partial tiles meet in LDS, are summed in wave order (deterministic)
 //    and go through the epilogue 4 columns per thread: the output itself when K is not split,
-//    else this slice's partial sums for splitk_reduce_kernel.
+//    else this slice's partial sums for the reduction pass (splitk_reduce_kernel, or
+//    splitk_resid_norm_kernel when the RMSNorm that follows rides along).
 constexpr int ST_BK = 128;
 
 template <int FN, int NS>
