@@ -38,10 +38,53 @@ void launch_embed(int dtype, const void* emb, const int* tokens, int M, int dim,
 
 // ---------------------------------------------------------------- RMSNorm
 // y = x / sqrt(mean(x^2) + eps) * w per row ("rms_norm" on the "Building llama3
-// from scratch" page), fp32 statistics, one rounding to the output dtype.
-template <typename TO>
+// from scratch" page), fp32 statistics, one rounding to the output dtype.  One 256-thread
+// workgroup per row; thread t holds float4 j of the row at element 4 (t + 256 j) in registers
+// (V4 of them, dim <= 1024 V4), so all of a row's loads, and the norm weight's, are in flight
+// together and x is read once.
+template <typename TO, int V4>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ w,
                                                       int dim, float eps, TO* __restrict__ y) {
+  __shared__ float red[8];
+  const int m = blockIdx.x;
+  const float* xr = x + (size_t)m * dim;
+  f32x4_t v[V4], g[V4];
+#pragma unroll
+  for (int j = 0; j < V4; ++j) {
+    const int i = (threadIdx.x + 256 * j) * 4;
+    v[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    g[j] = v[j];
+    if (i < dim) {
+      v[j] = *reinterpret_cast<const f32x4_t*>(xr + i);
+      g[j] = *reinterpret_cast<const f32x4_t*>(w + i);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < V4; ++j) ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+  ss = wave_sum(ss);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) red[wid] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tot += red[i];
+  const float inv = 1.0f / sqrtf(tot / (float)dim + eps);
+  TO* yr = y + (size_t)m * dim;
+#pragma unroll
+  for (int j = 0; j < V4; ++j) {
+    const int i = (threadIdx.x + 256 * j) * 4;
+    if (i < dim) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) yr[i + k] = from_f32<TO>(v[j][k] * inv * g[j][k]);
+    }
+  }
+}
+
+// Rows wider than the register version holds (dim > 16384): the same arithmetic in loops.
+template <typename TO>
+__global__ void __launch_bounds__(256) rmsnorm_loop_kernel(const float* __restrict__ x, const float* __restrict__ w,
+                                                           int dim, float eps, TO* __restrict__ y) {
   __shared__ float red[8];
   const int m = blockIdx.x;
   const float* xr = x + (size_t)m * dim;
@@ -67,13 +110,23 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
+template <typename TO>
+static void rmsnorm_dispatch(const float* x, const float* w, int M, int dim, float eps, TO* out, hipStream_t s) {
+  if (dim <= 1024) launch_k(rmsnorm_kernel<TO, 1>, M, 256, 0, s, x, w, dim, eps, out);
+  else if (dim <= 2048) launch_k(rmsnorm_kernel<TO, 2>, M, 256, 0, s, x, w, dim, eps, out);
+  else if (dim <= 4096) launch_k(rmsnorm_kernel<TO, 4>, M, 256, 0, s, x, w, dim, eps, out);
+  else if (dim <= 8192) launch_k(rmsnorm_kernel<TO, 8>, M, 256, 0, s, x, w, dim, eps, out);
+  else if (dim <= 16384) launch_k(rmsnorm_kernel<TO, 16>, M, 256, 0, s, x, w, dim, eps, out);
+  else launch_k(rmsnorm_loop_kernel<TO>, M, 256, 0, s, x, w, dim, eps, out);
+}
+
 void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, float eps, void* out,
                     hipStream_t s) {
   if (M <= 0) return;
   if (dtype == 1)
-    launch_k(rmsnorm_kernel<f16_t>, M, 256, 0, s, x, w, dim, eps, (f16_t*)out);
+    rmsnorm_dispatch(x, w, M, dim, eps, (f16_t*)out, s);
   else
-    launch_k(rmsnorm_kernel<float>, M, 256, 0, s, x, w, dim, eps, (float*)out);
+    rmsnorm_dispatch(x, w, M, dim, eps, (float*)out, s);
 }
 
 // ---------------------------------------------------------------- small helpers
