@@ -5,9 +5,10 @@
 // are rounded to fp16 rather than bf16: same bytes and MFMA rate, 8x finer
 // rounding, which keeps 32 layers within the bf16 parity bar.
 //
-// Two kernels share the tiling, fragment layout and epilogues: gemm_dma_kernel (the LDS-DMA
-// pipeline further below) serves every K % 32 == 0 shape but a batch's LM head, and the
-// register-staged gemm_f16_kernel described here serves the rest.  A third, gemm_stream_kernel,
+// Three kernels share the tiling, fragment layout and epilogues: gemm_dma_kernel (the LDS-DMA
+// pipeline further below, 32-wide stages) serves every K % 32 == 0 shape but a batch's LM head,
+// gemm_dma64_kernel (64-wide stages) takes its 256-row tiles when K % 64 == 0, and the
+// register-staged gemm_f16_kernel described here serves the rest.  A fourth, gemm_stream_kernel,
 // takes batches of 9 to 64 rows, which stream the weights.  launch_gemm_f16 at the end of the
 // file picks the kernel, tiles and K splits per shape.
 //
@@ -248,6 +249,55 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Epilogue of the DMA kernels: the wave's FM x FN accumulator blocks cover rows m0.. and columns
+// n0.. of the BM-row tile starting at row tm; smem holds at least BM x d floats for the RoPE rows.
+template <int BM, int FM, int FN, int NW, int EPI>
+__device__ __forceinline__ void dma_tile_epilogue(const EpiParams& ep, f32x4_t (&acc)[FM][FN], f16_t* smem, int M, int N,
+                                                  int tm, int m0, int n0, int tid, int lg, int l16) {
+  if constexpr (EPI == EPI_QKV) {
+    // Prefill rows only (positions pos0 + m, slot slot0, ranges checked by the host, and the
+    // table rows fit the stage buffers; the launcher sends other q|k|v projections to the
+    // register-staged kernel).  The tile stages its rows of the RoPE table (cos and sin, d/2
+    // each) in the idle LDS stage buffers with coalesced loads, so the epilogue reads hit LDS.
+    const int half = ep.head_dim >> 1;
+    __syncthreads();  // every wave is done with the stage buffers
+    float* s_cos = reinterpret_cast<float*>(smem);
+    float* s_sin = s_cos + BM * half;
+    const int rows = min(BM, M - tm);
+    for (int idx = tid; idx < rows * half; idx += NW * 64) {
+      const size_t src = (size_t)(ep.pos0 + tm) * half + idx;  // rows are consecutive positions
+      s_cos[idx] = ep.rope_cos[src];
+      s_sin[idx] = ep.rope_sin[src];
+    }
+    __syncthreads();
+    qkv_tile_epilogue<FM, FN, true>(ep, acc, M, N, m0, n0, lg, l16, s_cos, s_sin, tm);
+    return;
+  }
+  if constexpr (EPI == EPI_RESID) {
+    resid_tile_epilogue<FM, FN>(ep.out_f32, ep.ld, acc, M, N, m0, n0, lg, l16);
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + i * 16 + lg * 4 + r;
+        const int n = n0 + jn * 16 + l16;
+        const float v = acc[i][jn][r];
+        if (EPI == EPI_SWIGLU) {
+          const float vp = lane_xor1(v);
+          if (m < M && n < N && (n & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
+        } else if (m < M && n < N) {
+          if (EPI == EPI_STORE_F32) ep.out_f32[(size_t)blockIdx.y * M * ep.ld + (size_t)m * ep.ld + n] = v;
+          else ep.out_f32[(size_t)m * ep.ld + n] += v;
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int NS, int EPI, bool SCHED>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* __restrict__ A,
                                                                   const f16_t* __restrict__ W, int M, int N, int K,
@@ -409,48 +459,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(const f16_t* _
   }
 
 
-  if constexpr (EPI == EPI_QKV) {
-    // Prefill rows only (positions pos0 + m, slot slot0, ranges checked by the host, and the
-    // table rows fit the stage buffers; the launcher sends other q|k|v projections to the
-    // register-staged kernel).  The tile stages its rows of the RoPE table (cos and sin, d/2
-    // each) in the idle LDS stage buffers with coalesced loads, so the epilogue reads hit LDS.
-    const int half = ep.head_dim >> 1;
-    __syncthreads();  // every wave is done with the stage buffers
-    float* s_cos = reinterpret_cast<float*>(smem);
-    float* s_sin = s_cos + BM * half;
-    const int rows = min(BM, M - tm);
-    for (int idx = tid; idx < rows * half; idx += NW * 64) {
-      const size_t src = (size_t)(ep.pos0 + tm) * half + idx;  // rows are consecutive positions
-      s_cos[idx] = ep.rope_cos[src];
-      s_sin[idx] = ep.rope_sin[src];
-    }
-    __syncthreads();
-    qkv_tile_epilogue<FM, FN, true>(ep, acc, M, N, tm + wm * WM, tn + wn * WN, lg, l16, s_cos, s_sin, tm);
-    return;
-  }
-  if constexpr (EPI == EPI_RESID) {
-    resid_tile_epilogue<FM, FN>(ep.out_f32, ep.ld, acc, M, N, tm + wm * WM, tn + wn * WN, lg, l16);
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int jn = 0; jn < FN; ++jn) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = tm + wm * WM + i * 16 + lg * 4 + r;
-        const int n = tn + wn * WN + jn * 16 + l16;
-        const float v = acc[i][jn][r];
-        if (EPI == EPI_SWIGLU) {
-          const float vp = lane_xor1(v);
-          if (m < M && n < N && (n & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
-        } else if (m < M && n < N) {
-          if (EPI == EPI_STORE_F32) ep.out_f32[(size_t)blockIdx.y * M * ep.ld + (size_t)m * ep.ld + n] = v;
-          else ep.out_f32[(size_t)m * ep.ld + n] += v;
-        }
-      }
-    }
-  }
+  dma_tile_epilogue<BM, FM, FN, NW, EPI>(ep, acc, smem, M, N, tm, tm + wm * WM, tn + wn * WN, tid, lg, l16);
 }
 
 template <int BM, int BN, int WGM, int WGN, bool SB = false>
@@ -504,6 +513,216 @@ static int gemm_dma_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K
       break;
     case EPI_SWIGLU:
       launch_k(gemm_dma_kernel<BM, BN, WGM, WGN, NS, EPI_SWIGLU, SCHED>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      break;
+  }
+  return (int)grid.y;
+}
+
+// ------------------------------------------------------------------ 64-wide DMA stages
+//
+// As gemm_dma_kernel, with stages of BK = 64.  A tile row is then 128 bytes, one full cache line,
+// and a DMA instruction fills 8 whole rows; with the 64-byte rows of 32-wide stages every DMA
+// instruction touches 16 half lines, which doubles the cache requests per byte and keeps the
+// texture-address unit stalled on the vector cache for much of the kernel.  Two stage buffers:
+// while the waves multiply stage s, stage s+1 is landing; the DMA of stage s+2 goes out as soon as
+// every wave holds all of stage s in registers (after the barrier in the middle of iteration s),
+// so a stage has one whole iteration to land.  Chunk c of row r sits at c ^ (r % 8): the 8 lanes
+// of one LDS read cycle (8 consecutive rows, one chunk) hit distinct banks.  K must be a multiple
+// of 64 (and K slices even counts of 32-wide k-steps).
+
+constexpr int D64_BK = 64;
+
+__device__ __forceinline__ int d64_off(int r, int c) { return r * D64_BK + ((c ^ (r & 7)) << 3); }
+
+// One 16-byte-per-lane global -> LDS DMA from base + byte_off (uniform base, per-lane 32-bit
+// offset; lane l's bytes land at lds + 16 l), in asm so that the
+// compiler does not count it among the LDS operations: with the builtin, every later fragment
+// wait becomes a wait for all LDS reads.  Completion is tracked by the callers' explicit
+// vector-memory waits; M0 is declared clobbered, and one wait state follows its write.
+__device__ __forceinline__ void dma16_asm(const f16_t* base, unsigned byte_off, const f16_t* lds) {
+  const unsigned lds_addr =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const void __attribute__((address_space(3)))*)lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
+               "s"(lds_addr)
+               : "memory", "m0");
+}
+
+template <int BM, int BN, int WGM, int WGN, int EPI>
+__global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma64_kernel(const f16_t* __restrict__ A,
+                                                                    const f16_t* __restrict__ W, int M, int N, int K,
+                                                                    int tiles_m, int tiles_n, EpiParams ep,
+                                                                    int kb_per) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int STAGE = (BM + BN) * D64_BK;  // f16 elements per stage
+  constexpr int NI = (BM + BN) / 8;          // DMA instructions per stage
+  constexpr int PW = NI / NW;                // ... per wave
+  static_assert(NI % NW == 0 && PW < 64, "DMA instructions do not split evenly over the waves");
+
+  extern __shared__ __attribute__((aligned(16))) f16_t smem[];
+
+  int tm_idx, tn_idx;
+  dma_tile_of(blockIdx.x, tiles_m, tiles_n, tm_idx, tn_idx);
+  const int tm = tm_idx * BM, tn = tn_idx * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave offsets in SGPRs
+  const int wm = wid / WGN, wn = wid % WGN;
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  // K range of this workgroup: kb_per 32-wide k-steps (an even count) from split blockIdx.y.
+  const int kb0 = blockIdx.y * kb_per;
+  const int kbase = kb0 * DS_BK;
+
+  // Lane l of a DMA instruction takes row l / 8 of its 8-row block and physical chunk l % 8,
+  // which holds logical chunk (l % 8) ^ (row % 8).  The wave's first PA instructions fill A
+  // blocks, the rest W blocks; each keeps a 32-bit byte offset from the operand's base.
+  constexpr int PA = BM / 8 / NW;
+  static_assert((BM / 8) % NW == 0, "A blocks do not split evenly over the waves");
+  const int dr = lane >> 3;
+  const int dc = ((lane & 7) ^ dr) * 8;
+  unsigned goff[PW];
+  int dst_off[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int blk = wid + NW * i;  // 8-row block of the stage: A blocks first, then W blocks
+    if (i < PA) {
+      goff[i] = (unsigned)(((size_t)min(tm + blk * 8 + dr, M - 1) * K + kbase + dc) * sizeof(f16_t));
+      dst_off[i] = blk * 8 * D64_BK;
+    } else {
+      const int b = blk - BM / 8;
+      goff[i] = (unsigned)(((size_t)min(tn + b * 8 + dr, N - 1) * K + kbase + dc) * sizeof(f16_t));
+      dst_off[i] = BM * D64_BK + b * 8 * D64_BK;
+    }
+  }
+  auto issue = [&](int buf, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i)
+      dma16_asm(i < PA ? A : W, goff[i] + (unsigned)(k0 * sizeof(f16_t)), smem + buf * STAGE + dst_off[i]);
+  };
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn) acc[i][jn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Fragments of one 32-wide half of a stage (sub = 0 or 1), double-buffered in registers.
+  f16x8_t af[2][FM], bw[2][FN];
+  auto read_frags = [&](f16x8_t* a, f16x8_t* b, int buf, int sub) __attribute__((always_inline)) {
+    const f16_t* As = smem + buf * STAGE;
+    const f16_t* Bs = As + BM * D64_BK;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      a[i] = *reinterpret_cast<const f16x8_t*>(&As[d64_off(wm * WM + i * 16 + l16, sub * 4 + lg)]);
+#pragma unroll
+    for (int jn = 0; jn < FN; ++jn)
+      b[jn] = *reinterpret_cast<const f16x8_t*>(&Bs[d64_off(wn * WN + jn * 16 + l16, sub * 4 + lg)]);
+  };
+  auto mfmas = [&](const f16x8_t* a, const f16x8_t* b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < FN; ++jn)
+        acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[jn], acc[i][jn], 0, 0, 0);
+  };
+  // Interleave the half's fragment reads with its MFMAs.
+  auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < FM + FN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (FM * FN) / (FM + FN), 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN) * ((FM * FN) / (FM + FN)), 0);
+  };
+
+  const int ns = min(kb_per, K / DS_BK - kb0) / 2;
+  issue(0, 0);
+  if (ns > 1) {
+    issue(1, D64_BK);
+    wait_vmcnt<PW>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_frags(af[0], bw[0], 0, 0);
+  // Iteration st: first half on stage st's fragments 0..31 while reading 32..63; then, once
+  // stage st+1 has landed and every wave is past its reads of buffer st % 2, the DMA of stage
+  // st+2 into that buffer and the second half while reading stage st+1's first fragments.  The
+  // steady state (st + 2 < ns) has no branch; the last two iterations are peeled.
+  auto first_half = [&](int cur) __attribute__((always_inline)) {
+    read_frags(af[1], bw[1], cur, 1);
+    mfmas(af[0], bw[0]);
+    interleave();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  int st = 0;
+  for (; st + 2 < ns; ++st) {
+    const int cur = st & 1;
+    first_half(cur);
+    issue(cur, (st + 2) * D64_BK);
+    read_frags(af[0], bw[0], cur ^ 1, 0);
+    mfmas(af[1], bw[1]);
+    interleave();
+  }
+  if (st + 1 < ns) {
+    first_half(st & 1);
+    read_frags(af[0], bw[0], (st & 1) ^ 1, 0);
+    mfmas(af[1], bw[1]);
+    interleave();
+    ++st;
+  }
+  first_half(st & 1);
+  mfmas(af[1], bw[1]);
+
+  dma_tile_epilogue<BM, FM, FN, NW, EPI>(ep, acc, smem, M, N, tm, tm + wm * WM, tn + wn * WN, tid, lg, l16);
+}
+
+// Launches gemm_dma64_kernel; returns the number of K slices (K % 64 == 0).
+template <int BM, int BN, int WGM, int WGN>
+static int gemm_dma64_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep,
+                               hipStream_t s, int splits = 1) {
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const int nkb = K / DS_BK;
+  const int kb_per = splits > 1 ? 2 * ((((K + 63) / 64) + splits - 1) / splits) : nkb;
+  const dim3 grid(tm * tn, (nkb + kb_per - 1) / kb_per);
+  const int nt = 64 * WGM * WGN;
+  constexpr size_t lds = (size_t)2 * (BM + BN) * D64_BK * sizeof(f16_t);
+  static const bool attr = [] {
+    (void)hipFuncSetAttribute((const void*)gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_STORE_F32>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_RESID>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_QKV>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_SWIGLU>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    return true;
+  }();
+  (void)attr;
+  switch (ep.kind) {
+    case EPI_STORE_F32:
+      launch_k(gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_STORE_F32>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      break;
+    case EPI_RESID:
+      launch_k(gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_RESID>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      break;
+    case EPI_QKV:
+      // The staged RoPE rows (BM x d floats, d <= 128) fit square tiles only.
+      if constexpr (BM == BN)
+        launch_k(gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_QKV>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
+      else
+        gemm_dispatch<128, 128, 2, 2>(A, W, M, N, K, ep, s);
+      break;
+    case EPI_SWIGLU:
+      launch_k(gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_SWIGLU>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
   }
   return (int)grid.y;
@@ -953,8 +1172,11 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
       pe.kind = EPI_STORE_F32;
       pe.out_f32 = splitk_ws;
       pe.ld = N;
-      const int ns = bp.tile == 0 ? gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, pe, s, bp.splits)
-                                  : gemm_dma_dispatch<256, 128, 4, 2, 4, true>(a, w, M, N, K, pe, s, bp.splits);
+      const int ns = K % D64_BK == 0
+                         ? (bp.tile == 0 ? gemm_dma64_dispatch<256, 256, 2, 4>(a, w, M, N, K, pe, s, bp.splits)
+                                         : gemm_dma64_dispatch<256, 128, 4, 2>(a, w, M, N, K, pe, s, bp.splits))
+                         : (bp.tile == 0 ? gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, pe, s, bp.splits)
+                                         : gemm_dma_dispatch<256, 128, 4, 2, 4, true>(a, w, M, N, K, pe, s, bp.splits));
       reduce(ns);
       return;
     }
@@ -1011,14 +1233,18 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
     }
   }
   if (M > 64 && K % DS_BK == 0 && (!qkv || dma_qkv_ok)) {
-    if (M > 128 && tiles(256, 256) >= 192)
-      gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
-    else if (M > 128 && !qkv && tiles(256, 128) >= 192)
-      gemm_dma_dispatch<256, 128, 4, 2, 4, true>(a, w, M, N, K, ep, s);
-    else if (M > 64 && tiles(128, 128) >= 192)
+    // The big tiles take 64-wide stages when K allows (whole cache lines per DMA row).
+    if (M > 128 && tiles(256, 256) >= 192) {
+      if (K % D64_BK == 0) gemm_dma64_dispatch<256, 256, 2, 4>(a, w, M, N, K, ep, s);
+      else gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
+    } else if (M > 128 && !qkv && tiles(256, 128) >= 192) {
+      if (K % D64_BK == 0) gemm_dma64_dispatch<256, 128, 4, 2>(a, w, M, N, K, ep, s);
+      else gemm_dma_dispatch<256, 128, 4, 2, 4, true>(a, w, M, N, K, ep, s);
+    } else if (M > 64 && tiles(128, 128) >= 192) {
       gemm_dma_dispatch<128, 128, 2, 2, 4>(a, w, M, N, K, ep, s);
-    else
+    } else {
       gemm_dma_dispatch<64, 64, 2, 2, 4>(a, w, M, N, K, ep, s);
+    }
     return;
   }
   // The q|k|v epilogue (RoPE table reads, cache addressing) does not fit the register-staged
