@@ -627,12 +627,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma64_kernel(const f16_t*
       for (int jn = 0; jn < FN; ++jn)
         acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[jn], acc[i][jn], 0, 0, 0);
   };
-  // Interleave the half's fragment reads with its MFMAs.
+  // Interleave the half's fragment reads with its MFMAs, products first: the first MFMA then
+  // waits only for reads issued in the previous half.
   auto interleave = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < FM + FN; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, (FM * FN) / (FM + FN), 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN) * ((FM * FN) / (FM + FN)), 0);
   };
