@@ -538,7 +538,9 @@ __device__ __forceinline__ int d64_off(int r, int c) { return r * D64_BK + ((c ^
 // offset; lane l's bytes land at lds + 16 l), in asm so that the
 // compiler does not count it among the LDS operations: with the builtin, every later fragment
 // wait becomes a wait for all LDS reads.  Completion is tracked by the callers' explicit
-// vector-memory waits; M0 is declared clobbered, and one wait state follows its write.
+// vector-memory waits, and one wait state follows the M0 write.  The compiler reserves M0 and
+// need not honour it on a clobber list, so this is for kernels in which nothing else uses M0:
+// gemm_dma64_kernel's code has no other M0 access (checked in its ISA).
 __device__ __forceinline__ void dma16_asm(const f16_t* base, unsigned byte_off, const f16_t* lds) {
   const unsigned lds_addr =
       __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const void __attribute__((address_space(3)))*)lds);
