@@ -688,6 +688,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma64_kernel(const f16_t*
   dma_tile_epilogue<BM, FM, FN, NW, EPI>(ep, acc, smem, M, N, tm, tm + wm * WM, tn + wn * WN, tid, lg, l16);
 }
 
+// Whether a projection can take gemm_dma64_kernel: K a multiple of 64, and every operand byte
+// within the 32-bit lane offset its DMA addresses with (kept under 2 GiB).
+static bool dma64_ok(int M, int N, int K) {
+  return K % D64_BK == 0 && (size_t)std::max(M, N) * (size_t)K * sizeof(f16_t) < ((size_t)1 << 31);
+}
+
 // Launches gemm_dma64_kernel; returns the number of K slices (K % 64 == 0).
 template <int BM, int BN, int WGM, int WGN>
 static int gemm_dma64_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K, const EpiParams& ep,
@@ -1175,7 +1181,7 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
       pe.kind = EPI_STORE_F32;
       pe.out_f32 = splitk_ws;
       pe.ld = N;
-      const int ns = K % D64_BK == 0
+      const int ns = dma64_ok(M, N, K)
                          ? (bp.tile == 0 ? gemm_dma64_dispatch<256, 256, 2, 4>(a, w, M, N, K, pe, s, bp.splits)
                                          : gemm_dma64_dispatch<256, 128, 4, 2>(a, w, M, N, K, pe, s, bp.splits))
                          : (bp.tile == 0 ? gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, pe, s, bp.splits)
@@ -1238,10 +1244,10 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
   if (M > 64 && K % DS_BK == 0 && (!qkv || dma_qkv_ok)) {
     // The big tiles take 64-wide stages when K allows (whole cache lines per DMA row).
     if (M > 128 && tiles(256, 256) >= 192) {
-      if (K % D64_BK == 0) gemm_dma64_dispatch<256, 256, 2, 4>(a, w, M, N, K, ep, s);
+      if (dma64_ok(M, N, K)) gemm_dma64_dispatch<256, 256, 2, 4>(a, w, M, N, K, ep, s);
       else gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
     } else if (M > 128 && !qkv && tiles(256, 128) >= 192) {
-      if (K % D64_BK == 0) gemm_dma64_dispatch<256, 128, 4, 2>(a, w, M, N, K, ep, s);
+      if (dma64_ok(M, N, K)) gemm_dma64_dispatch<256, 128, 4, 2>(a, w, M, N, K, ep, s);
       else gemm_dma_dispatch<256, 128, 4, 2, 4, true>(a, w, M, N, K, ep, s);
     } else if (M > 64 && tiles(128, 128) >= 192) {
       gemm_dma_dispatch<128, 128, 2, 2, 4>(a, w, M, N, K, ep, s);
