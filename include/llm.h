@@ -20,14 +20,25 @@
  *    llm_init_weights.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every compute call only enqueues work on that stream and returns; results
- *    are valid once the stream has been synchronised.  No call synchronises the
- *    device except llm_init_weights (at its end) and llm_read_device_error.
+ *    are valid once the stream has been synchronised.  No call waits for the
+ *    device except llm_init_weights (it synchronises `stream` at its end),
+ *    llm_read_device_error (it synchronises `stream`) and the diagnostics
+ *    llm_set_kernel_timing / llm_kernel_timing (they wait for the timing events
+ *    already recorded).
  *  - Matrices are row-major.  Weights are [out_features, in_features] and a
  *    linear layer computes y = x W^T (printed shapes on the "Building llama3
  *    from scratch" page: wq [4096, 4096], wk/wv [1024, 4096]).  Query head h
  *    owns rows h*head_dim .. h*head_dim+head_dim-1 of wq (per-head view of wq on
  *    the same page); K/V head g likewise owns rows of wk/wv.
- *  - bf16 buffers hold raw bfloat16 bit patterns (uint16).
+ *  - Element types.  An LLM_F32 model takes fp32 weights and computes and
+ *    stores everything in fp32.  An LLM_BF16 model takes its weights as raw
+ *    bfloat16 bit patterns (uint16); llm_init_weights converts them to fp16
+ *    (IEEE binary16) in the packed buffer, and its activations and KV cache are
+ *    fp16 too, with fp32 accumulation, an fp32 residual stream and fp32 logits.
+ *    The conversion is exact for every bf16 weight whose magnitude lies in
+ *    [2^-14, 65504]; smaller magnitudes lose low bits, larger ones raise
+ *    LLM_DEVERR_RANGE (as does any fp16 activation or cache value that leaves
+ *    fp16's finite range).
  *  - Every call returns an llm_status.  Host-side validation happens before
  *    anything is enqueued, so a failing call leaves the stream untouched.
  *    llm_last_error_message() then describes the failure (thread-local).
@@ -52,25 +63,36 @@ typedef enum llm_status {
   LLM_ERR_CONFIG = -2,           /* inconsistent hyper-parameters */
   LLM_ERR_OUT_OF_RANGE = -3,     /* positions / slots / batch beyond the configured maxima */
   LLM_ERR_BUFFER_TOO_SMALL = -4, /* a caller buffer is smaller than the size query returns */
-  LLM_ERR_HIP = -5               /* a HIP runtime call failed */
+  LLM_ERR_HIP = -5,              /* a HIP runtime call failed */
+  /* Not a status: makes every int32 value a valid llm_status, so that a status read from
+   * elsewhere (llm_status_string of an unknown code) is defined behaviour in C++ too. */
+  LLM_STATUS_MAX_ENUM = 0x7FFFFFFF
 } llm_status;
 
-/* Storage type of weights, activations and the KV cache. */
+/* Type of the weights handed to llm_init_weights: LLM_F32 (fp32 everywhere) or
+ * LLM_BF16 (bf16 weights, held and computed as fp16; see "Element types" above). */
 enum { LLM_F32 = 0, LLM_BF16 = 1 };
 
-/* Device-side error flags (bit mask) reported by llm_read_device_error. */
-enum { LLM_DEVERR_TOKEN = 1, LLM_DEVERR_POSITION = 2, LLM_DEVERR_SLOT = 4 };
+/* Device-side error flags (bit mask) reported by llm_read_device_error:
+ * TOKEN a token id outside [0, vocab_size); POSITION a decode position outside
+ * [0, max_seq_len); SLOT a decode slot outside [0, max_batch); RANGE a value
+ * stored as fp16 (a packed weight, a normalised activation, q/k/v, a KV-cache
+ * entry or a SwiGLU output) fell outside fp16's finite range or was NaN. */
+enum { LLM_DEVERR_TOKEN = 1, LLM_DEVERR_POSITION = 2, LLM_DEVERR_SLOT = 4, LLM_DEVERR_RANGE = 8 };
 
 /*
  * Model hyper-parameters: the params.json field set printed on the "Building
  * llama3 from scratch" page (dim, n_layers, n_heads, n_kv_heads, vocab_size,
  * norm_eps, rope_theta) with the feed-forward width given explicitly instead of
  * multiple_of / ffn_dim_multiplier, plus the context length (max_seq_len, NumPy
- * page, "Struktur").  Requirements: dim % n_heads == 0; head_dim = dim/n_heads
- * is a multiple of 16; n_heads % n_kv_heads == 0; dim and ffn_hidden_dim are
- * multiples of 8 (bf16) or 4 (fp32).
+ * page, "Struktur").  Requirements (llm_check_config): every size positive;
+ * dim % n_heads == 0 and head_dim = dim / n_heads is 48, 64 or 128;
+ * n_heads % n_kv_heads == 0 and n_heads / n_kv_heads is at most 4 or a multiple
+ * of 4; dim and ffn_hidden_dim are multiples of 8; rope_theta > 0; norm_eps >= 0;
+ * 1 <= max_batch <= 1024; max_seq_len <= 2^20 and max_seq_len * max_batch <= 2^31.
  * max_batch: number of KV-cache slots (= largest decode batch).
- * max_prefill_tokens: largest n_tokens of one llm_prefill / llm_layer_forward.
+ * max_prefill_tokens: largest n_tokens of one llm_prefill / llm_layer_forward, and
+ * the largest total of one llm_prefill_batch.
  */
 typedef struct llm_config {
   int32_t dim;
@@ -120,10 +142,14 @@ typedef struct llm_model llm_model;
 llm_status llm_check_config(const llm_config* cfg);
 
 /* Sizes in bytes of the three device buffers llm_init_weights needs (0 if the
- * config is invalid).  Packed weights: every weight plus the fp32 RoPE tables.
- * KV cache: n_layers x {K,V} x max_batch x n_kv_heads x max_seq_len x head_dim.
- * Workspace: activations for max(max_prefill_tokens, max_batch) rows and
- * attention / argmax partials. */
+ * config is invalid).  Packed weights: every weight (fp16 for LLM_BF16, fp32 for
+ * LLM_F32) plus the fp32 norm weights and RoPE tables.
+ * KV cache: row-major [n_layers][2 (K, V)][max_batch (slot)][n_kv_heads]
+ * [max_seq_len][head_dim] of fp16 (LLM_BF16) or fp32 (LLM_F32) elements; K is
+ * stored after RoPE.  A caller may fill a slot's first positions directly (a
+ * cache built elsewhere) and continue it with llm_decode_step or llm_prefill.
+ * Workspace: activations for max(max_prefill_tokens, max_batch) rows, attention,
+ * split-K and argmax partials, and batched-prefill descriptors. */
 size_t llm_packed_weight_bytes(const llm_config* cfg);
 size_t llm_kv_cache_bytes(const llm_config* cfg);
 size_t llm_workspace_bytes(const llm_config* cfg);
@@ -135,10 +161,11 @@ size_t llm_workspace_bytes(const llm_config* cfg);
  * from an fp64 outer product, "RoPE #1" on the NumPy page) and create a model
  * handle in *out.  The three buffers must stay alive until llm_free; the
  * source weights may be freed once this call returns.  The handle also owns a
- * small pinned host staging buffer (per-row metadata of llm_prefill_batch), a
- * capture stream and events, released by llm_free.  The call synchronises
- * `stream` before returning.  Errors: INVALID_ARG (null pointer), CONFIG,
- * BUFFER_TOO_SMALL (a size below the corresponding query), HIP.
+ * capture stream, events and graphs, released by llm_free.  The call clears the
+ * device error flags and synchronises `stream` before returning; a weight that
+ * does not fit fp16 shows as LLM_DEVERR_RANGE in llm_read_device_error.
+ * Errors: INVALID_ARG (null pointer), CONFIG, BUFFER_TOO_SMALL (a size below the
+ * corresponding query), HIP.
  */
 llm_status llm_init_weights(const llm_config* cfg, const llm_weights* weights,
                             void* packed, size_t packed_bytes,
@@ -165,8 +192,11 @@ llm_status llm_prefill(llm_model* m, int32_t slot, const int32_t* tokens_dev, in
  * cache slot slots_host[b] (positions before starts_host[b] must already be in that
  * slot's cache).  logits_dev (device fp32 [batch][vocab]) receives the logits of
  * each sequence's last position.  The three host arrays (batch entries each) are
- * read during the call; projections run once over all rows, attention per
- * sequence.  Results equal separate llm_prefill calls up to rounding.  Errors:
+ * read during the call and travel to the device inside kernel arguments, so the
+ * call neither stages them in host memory nor waits for the device; they may be
+ * reused as soon as it returns.  Projections run once over all rows, and the
+ * attention of every sequence runs in one launch.  Results equal separate
+ * llm_prefill calls up to rounding.  Errors:
  * INVALID_ARG (null pointer, batch < 1, a length < 1, two sequences with the same
  * slot), OUT_OF_RANGE (batch > max_batch, a slot >= max_batch, start + length >
  * max_seq_len, total tokens > max_prefill_tokens), HIP.
@@ -231,19 +261,19 @@ llm_status llm_read_device_error(llm_model* m, int32_t* flags, void* stream);
  * instead of replaying its graph.  Kernels are charged to LLM_K_* groups (one
  * group invocation may launch several kernels, e.g. a split-K GEMM and its
  * reduce pass).  Enabling resets the totals.  llm_kernel_timing synchronises on
- * the recorded events and returns, for one group, the number of invocations
- * and the summed kernel execution time in milliseconds.  Errors: INVALID_ARG,
- * HIP.
+ * the recorded events and returns, for one group, the number of invocations,
+ * the number of kernels they dispatched (`kernels` may be NULL) and the summed
+ * kernel execution time in milliseconds.  Errors: INVALID_ARG, HIP.
  */
 enum {
   LLM_K_EMBED = 0, LLM_K_RMSNORM = 1, LLM_K_QKV = 2, LLM_K_ATTN = 3, LLM_K_WO = 4,
   LLM_K_GATE_UP = 5, LLM_K_DOWN = 6, LLM_K_LM_HEAD = 7, LLM_K_ARGMAX = 8, LLM_K_COUNT = 9
 };
 llm_status llm_set_kernel_timing(llm_model* m, int32_t enable);
-llm_status llm_kernel_timing(llm_model* m, int32_t kind, int64_t* launches, double* total_ms);
+llm_status llm_kernel_timing(llm_model* m, int32_t kind, int64_t* launches, int64_t* kernels, double* total_ms);
 
-/* Release the handle and what it owns on the host (staging buffer, stream,
- * events, graphs); no caller-provided device memory is freed.  NULL is allowed. */
+/* Release the handle and what it owns on the host (stream, events, graphs); no
+ * caller-provided device memory is freed.  NULL is allowed. */
 void llm_free(llm_model* m);
 
 const char* llm_status_string(llm_status s);

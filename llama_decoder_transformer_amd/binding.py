@@ -23,7 +23,7 @@ LLM_F32 = 0
 LLM_BF16 = 1
 STATUS = {0: "LLM_OK", -1: "LLM_ERR_INVALID_ARG", -2: "LLM_ERR_CONFIG", -3: "LLM_ERR_OUT_OF_RANGE",
           -4: "LLM_ERR_BUFFER_TOO_SMALL", -5: "LLM_ERR_HIP"}
-DEVERR_TOKEN, DEVERR_POSITION, DEVERR_SLOT = 1, 2, 4
+DEVERR_TOKEN, DEVERR_POSITION, DEVERR_SLOT, DEVERR_RANGE = 1, 2, 4, 8
 
 EXPORTED = ("llm_check_config", "llm_packed_weight_bytes", "llm_kv_cache_bytes", "llm_workspace_bytes",
             "llm_init_weights", "llm_prefill", "llm_prefill_batch", "llm_layer_forward", "llm_decode_step",
@@ -87,7 +87,8 @@ def lib():
                                        c_void_p, c_void_p]),
             "llm_read_device_error": (c_int32, [c_void_p, POINTER(c_int32), c_void_p]),
             "llm_set_kernel_timing": (c_int32, [c_void_p, c_int32]),
-            "llm_kernel_timing": (c_int32, [c_void_p, c_int32, POINTER(ctypes.c_int64), POINTER(ctypes.c_double)]),
+            "llm_kernel_timing": (c_int32, [c_void_p, c_int32, POINTER(ctypes.c_int64), POINTER(ctypes.c_int64),
+                                            POINTER(ctypes.c_double)]),
             "llm_free": (None, [c_void_p]),
             "llm_status_string": (c_char_p, [c_int32]),
             "llm_last_error_message": (c_char_p, []),
@@ -189,10 +190,18 @@ def llm_set_kernel_timing(handle: int, enable: bool) -> None:
 
 
 def llm_kernel_timing(handle: int, kind: int) -> tuple[int, float]:
+    """(invocations, total kernel ms) of one kernel group."""
+    n, _, ms = llm_kernel_timing_full(handle, kind)
+    return n, ms
+
+
+def llm_kernel_timing_full(handle: int, kind: int) -> tuple[int, int, float]:
+    """(invocations, kernels dispatched, total kernel ms) of one kernel group."""
     n = ctypes.c_int64(0)
+    k = ctypes.c_int64(0)
     ms = ctypes.c_double(0.0)
-    _check(lib().llm_kernel_timing(handle, kind, ctypes.byref(n), ctypes.byref(ms)))
-    return n.value, ms.value
+    _check(lib().llm_kernel_timing(handle, kind, ctypes.byref(n), ctypes.byref(k), ctypes.byref(ms)))
+    return n.value, k.value, ms.value
 
 
 def llm_free(handle: int) -> None:

@@ -402,6 +402,11 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 // scaled probabilities, packed to fp16, are already the B operand of
 // O^T += V^T P^T (details at the kernel).
 //
+// A batched prefill runs all its sequences in one launch: the grid's x index is a
+// flat list of (sequence, query block) work items, taken from the last (the
+// heaviest blocks of the last sequence) to the first, and each workgroup finds its
+// sequence by a binary search over the descriptors' first-block indices.
+//
 // K/V tiles are double-buffered in LDS: the next tile's global loads are issued
 // into registers before the current tile's math, stored after it, and a single
 // barrier per tile separates the two buffers' uses.  The causal mask is applied
@@ -445,7 +450,8 @@ __device__ __forceinline__ uint2 pf_read_tr(const f16_t* lds_elem) {
 template <int HPW, int NW>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, const f16_t* __restrict__ vc,
-                      int slot, int pos0, int S, int H, int G, int max_seq, f16_t* __restrict__ out) {
+                      int slot_arg, int pos0_arg, int S_arg, int H, int G, int max_seq, f16_t* __restrict__ out,
+                      const SeqDesc* __restrict__ seqs, int nseq) {
   typedef float f32x16_t __attribute__((ext_vector_type(16)));
   constexpr int QSUB = NW / HPW;  // 32-query sub-blocks per workgroup
   constexpr int QB = 32 * QSUB;
@@ -459,13 +465,29 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
   const int l32 = lane & 31, lh = lane >> 5;
   const int hpg = H / G;
   const int nhb = hpg / HPW;
-  const int qblk = gridDim.x - 1 - blockIdx.x;
+  const int ld_q = H * PF_D;
+  int qblk = gridDim.x - 1 - blockIdx.x;
+  int slot = slot_arg, pos0 = pos0_arg, S = S_arg;
+  if (seqs) {
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seqs[mid].blk0 <= qblk) lo = mid;
+      else hi = mid - 1;
+    }
+    const SeqDesc sd = seqs[lo];
+    qblk -= sd.blk0;
+    slot = sd.slot;
+    pos0 = sd.start;
+    S = sd.n;
+    q += (size_t)sd.row0 * ld_q;
+    out += (size_t)sd.row0 * ld_q;
+  }
   const int g = blockIdx.y / nhb;
   const int head = g * hpg + (blockIdx.y % nhb) * HPW + (wid % HPW);
   const int qw0 = qblk * QB + 32 * (wid / HPW);
   const int wg_last = min(S, qblk * QB + QB) - 1;
   const int kv_end = pos0 + wg_last + 1;
-  const int ld_q = H * PF_D;
   const float scale = LOG2E_F / sqrtf((float)PF_D);
 
   // Q^T fragments (B operand): column = query l32, k = dims 16 s + 8 lh .. +7.
@@ -860,34 +882,42 @@ bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads) {
 
 template <int HPW, int NW>
 static void attn_prefill_launch(dim3 grid, hipStream_t s, const f16_t* q, const f16_t* k, const f16_t* v, int slot,
-                                  int pos0, int n_tokens, int H, int G, int max_seq, f16_t* out) {
+                                  int pos0, int n_tokens, int H, int G, int max_seq, f16_t* out,
+                                  const SeqDesc* seqs, int nseq) {
   // The double-buffered tiles exceed the default 64 KiB dynamic LDS limit, raised once (a
   // function-local static is initialised exactly once even with concurrent callers).
   static const hipError_t attr = hipFuncSetAttribute((const void*)attn_prefill_kernel<HPW, NW>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)PF_LDS_BYTES);
   (void)attr;
   launch_k(attn_prefill_kernel<HPW, NW>, grid, 64 * NW, PF_LDS_BYTES, s, q, k, v, slot, pos0, n_tokens, H, G, max_seq,
-           out);
+           out, seqs, nseq);
 }
 
-void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0, int n_tokens,
-                         int n_heads, int n_kv_heads, int head_dim, int max_seq, void* out, hipStream_t s) {
-  if (n_tokens <= 0) return;
-  (void)head_dim;
+// Waves per workgroup: nw / hpw sub-blocks of 32 queries share each K/V tile.  8 waves halve
+// the tile fills per query but make each causal block heavier; measured on MI355X at the
+// Llama-3-8B shape: S = 2048 attention 85-88 us with 8 waves against 95 with 4, S = 8192 836
+// against 739-767.
+static int attn_prefill_waves(int max_n) { return max_n <= 4096 ? 8 : 4; }
+
+int attn_prefill_block_rows(int max_n, int n_heads, int n_kv_heads) {
   const int hpg = n_heads / n_kv_heads;
   const int hpw = hpg >= 4 ? 4 : hpg;
-  // Waves per workgroup: nw / hpw sub-blocks of 32 queries share each K/V tile.  8 waves halve
-  // the tile fills per query but make each causal block heavier; measured on MI355X at the
-  // Llama-3-8B shape: S = 2048 attention 85-88 us with 8 waves against 95 with 4, S = 8192 836
-  // against 739-767.
-  const int nw = n_tokens <= 4096 ? 8 : 4;
-  const int qb = 32 * (nw / hpw);
-  dim3 grid((n_tokens + qb - 1) / qb, n_kv_heads * (hpg / hpw));
+  return 32 * (attn_prefill_waves(max_n) / hpw);
+}
+
+static void attn_prefill_any(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0,
+                             int n_tokens, int max_n, int n_blocks, const SeqDesc* seqs, int nseq, int n_heads,
+                             int n_kv_heads, int max_seq, void* out, hipStream_t s) {
+  const int hpg = n_heads / n_kv_heads;
+  const int hpw = hpg >= 4 ? 4 : hpg;
+  const int nw = attn_prefill_waves(max_n);
+  dim3 grid(n_blocks, n_kv_heads * (hpg / hpw));
   const f16_t* qq = (const f16_t*)q;
   const f16_t* kk = (const f16_t*)k_cache;
   const f16_t* vv = (const f16_t*)v_cache;
   f16_t* oo = (f16_t*)out;
-#define LLM_PF(HPW, NW) attn_prefill_launch<HPW, NW>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo)
+#define LLM_PF(HPW, NW) \
+  attn_prefill_launch<HPW, NW>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo, seqs, nseq)
   if (nw == 8) {
     if (hpw == 4) LLM_PF(4, 8);
     else if (hpw == 2) LLM_PF(2, 8);
@@ -898,6 +928,23 @@ void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache
     else LLM_PF(1, 4);
   }
 #undef LLM_PF
+}
+
+void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0, int n_tokens,
+                         int n_heads, int n_kv_heads, int head_dim, int max_seq, void* out, hipStream_t s) {
+  if (n_tokens <= 0) return;
+  (void)head_dim;
+  const int qb = attn_prefill_block_rows(n_tokens, n_heads, n_kv_heads);
+  attn_prefill_any(q, k_cache, v_cache, slot, pos0, n_tokens, n_tokens, (n_tokens + qb - 1) / qb, nullptr, 0, n_heads,
+                   n_kv_heads, max_seq, out, s);
+}
+
+void launch_attn_prefill_varlen(const void* q, const void* k_cache, const void* v_cache, const SeqDesc* seqs,
+                                int nseq, int n_blocks, int max_n, int n_heads, int n_kv_heads, int head_dim,
+                                int max_seq, void* out, hipStream_t s) {
+  if (nseq <= 0 || n_blocks <= 0) return;
+  (void)head_dim;
+  attn_prefill_any(q, k_cache, v_cache, 0, 0, 0, max_n, n_blocks, seqs, nseq, n_heads, n_kv_heads, max_seq, out, s);
 }
 
 }  // namespace llm

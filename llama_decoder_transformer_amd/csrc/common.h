@@ -16,6 +16,19 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 
+// Device error bit (LLM_DEVERR_RANGE in llm.h): a value stored as fp16 was outside fp16's
+// finite range (it became +-inf) or was not a number.
+constexpr int LLM_DEVERR_RANGE_BIT = 8;
+
+// True when fp16(v) is not finite: |v| rounds past the largest fp16 value (65504) or v is NaN.
+__device__ __forceinline__ bool f16_out_of_range(float v) { return !(__builtin_fabsf(v) < 65520.0f); }
+
+// Range check of a value about to be stored in the activation dtype (only fp16 can overflow).
+template <typename T> __device__ __forceinline__ bool store_out_of_range(float v) {
+  if constexpr (__is_same(T, f16_t)) return f16_out_of_range(v);
+  else return false;
+}
+
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }

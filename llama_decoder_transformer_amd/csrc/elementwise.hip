@@ -44,7 +44,7 @@ void launch_embed(int dtype, const void* emb, const int* tokens, int M, int dim,
 // together and x is read once.
 template <typename TO, int V4>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x, const float* __restrict__ w,
-                                                      int dim, float eps, TO* __restrict__ y) {
+                                                      int dim, float eps, TO* __restrict__ y, int* err) {
   __shared__ float red[8];
   const int m = blockIdx.x;
   const float* xr = x + (size_t)m * dim;
@@ -71,20 +71,26 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   for (int i = 0; i < 4; ++i) tot += red[i];
   const float inv = 1.0f / sqrtf(tot / (float)dim + eps);
   TO* yr = y + (size_t)m * dim;
+  bool bad = false;
 #pragma unroll
   for (int j = 0; j < V4; ++j) {
     const int i = (threadIdx.x + 256 * j) * 4;
     if (i < dim) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) yr[i + k] = from_f32<TO>(v[j][k] * inv * g[j][k]);
+      for (int k = 0; k < 4; ++k) {
+        const float o = v[j][k] * inv * g[j][k];
+        bad |= store_out_of_range<TO>(o);
+        yr[i + k] = from_f32<TO>(o);
+      }
     }
   }
+  if (bad) atomicOr(err, LLM_DEVERR_RANGE_BIT);
 }
 
 // Rows wider than the register version holds (dim > 16384): the same arithmetic in loops.
 template <typename TO>
 __global__ void __launch_bounds__(256) rmsnorm_loop_kernel(const float* __restrict__ x, const float* __restrict__ w,
-                                                           int dim, float eps, TO* __restrict__ y) {
+                                                           int dim, float eps, TO* __restrict__ y, int* err) {
   __shared__ float red[8];
   const int m = blockIdx.x;
   const float* xr = x + (size_t)m * dim;
@@ -102,31 +108,38 @@ __global__ void __launch_bounds__(256) rmsnorm_loop_kernel(const float* __restri
   for (int i = 0; i < 4; ++i) tot += red[i];
   const float inv = 1.0f / sqrtf(tot / (float)dim + eps);
   TO* yr = y + (size_t)m * dim;
+  bool bad = false;
   for (int i = threadIdx.x * 4; i < dim; i += 256 * 4) {
     f32x4_t v = *reinterpret_cast<const f32x4_t*>(xr + i);
     f32x4_t g = *reinterpret_cast<const f32x4_t*>(w + i);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) yr[i + k] = from_f32<TO>(v[k] * inv * g[k]);
+    for (int k = 0; k < 4; ++k) {
+      const float o = v[k] * inv * g[k];
+      bad |= store_out_of_range<TO>(o);
+      yr[i + k] = from_f32<TO>(o);
+    }
   }
+  if (bad) atomicOr(err, LLM_DEVERR_RANGE_BIT);
 }
 
 template <typename TO>
-static void rmsnorm_dispatch(const float* x, const float* w, int M, int dim, float eps, TO* out, hipStream_t s) {
-  if (dim <= 1024) launch_k(rmsnorm_kernel<TO, 1>, M, 256, 0, s, x, w, dim, eps, out);
-  else if (dim <= 2048) launch_k(rmsnorm_kernel<TO, 2>, M, 256, 0, s, x, w, dim, eps, out);
-  else if (dim <= 4096) launch_k(rmsnorm_kernel<TO, 4>, M, 256, 0, s, x, w, dim, eps, out);
-  else if (dim <= 8192) launch_k(rmsnorm_kernel<TO, 8>, M, 256, 0, s, x, w, dim, eps, out);
-  else if (dim <= 16384) launch_k(rmsnorm_kernel<TO, 16>, M, 256, 0, s, x, w, dim, eps, out);
-  else launch_k(rmsnorm_loop_kernel<TO>, M, 256, 0, s, x, w, dim, eps, out);
+static void rmsnorm_dispatch(const float* x, const float* w, int M, int dim, float eps, TO* out, int* err,
+                             hipStream_t s) {
+  if (dim <= 1024) launch_k(rmsnorm_kernel<TO, 1>, M, 256, 0, s, x, w, dim, eps, out, err);
+  else if (dim <= 2048) launch_k(rmsnorm_kernel<TO, 2>, M, 256, 0, s, x, w, dim, eps, out, err);
+  else if (dim <= 4096) launch_k(rmsnorm_kernel<TO, 4>, M, 256, 0, s, x, w, dim, eps, out, err);
+  else if (dim <= 8192) launch_k(rmsnorm_kernel<TO, 8>, M, 256, 0, s, x, w, dim, eps, out, err);
+  else if (dim <= 16384) launch_k(rmsnorm_kernel<TO, 16>, M, 256, 0, s, x, w, dim, eps, out, err);
+  else launch_k(rmsnorm_loop_kernel<TO>, M, 256, 0, s, x, w, dim, eps, out, err);
 }
 
-void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, float eps, void* out,
+void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, float eps, void* out, int* err,
                     hipStream_t s) {
   if (M <= 0) return;
   if (dtype == 1)
-    rmsnorm_dispatch(x, w, M, dim, eps, (f16_t*)out, s);
+    rmsnorm_dispatch(x, w, M, dim, eps, (f16_t*)out, err, s);
   else
-    rmsnorm_dispatch(x, w, M, dim, eps, (float*)out, s);
+    rmsnorm_dispatch(x, w, M, dim, eps, (float*)out, err, s);
 }
 
 // ---------------------------------------------------------------- small helpers
@@ -145,23 +158,32 @@ void launch_to_f32(int dtype, const void* src, float* dst, size_t n, hipStream_t
     launch_k(to_f32_kernel<float>, g, 256, 0, s, (const float*)src, dst, n);
 }
 
-// Weight packing for the bf16-weight path: rows of a bf16 matrix are widened and
-// stored as fp16 (round to nearest even; exact for every bf16 value whose
-// magnitude lies in fp16's normal range) at destination row r * row_mult + row_off.
+// Weight packing for the bf16-weight path: rows of a bf16 matrix are stored as fp16
+// (round to nearest even) at destination row r * row_mult + row_off.  The conversion
+// is exact for bf16 values whose magnitude lies in fp16's normal range
+// [2^-14, 65504]; smaller magnitudes keep fewer significant bits (fp16 subnormals),
+// and a magnitude above 65504 (or a non-finite weight) becomes +-inf and raises
+// LLM_DEVERR_RANGE.
 __global__ void pack_rows_kernel(const bf16_t* __restrict__ src, f16_t* __restrict__ dst, size_t rows, int cols,
-                                 int row_mult, int row_off) {
+                                 int row_mult, int row_off, int* err) {
   const size_t n = rows * (size_t)cols;
+  bool bad = false;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
     const size_t r = i / cols, c = i % cols;
-    dst[(r * row_mult + row_off) * (size_t)cols + c] = (f16_t)bf16_to_f32(src[i]);
+    const float v = bf16_to_f32(src[i]);
+    bad |= f16_out_of_range(v);
+    dst[(r * row_mult + row_off) * (size_t)cols + c] = (f16_t)v;
   }
+  if (bad) atomicOr(err, LLM_DEVERR_RANGE_BIT);
 }
 
-void launch_pack_rows(const void* src, void* dst, size_t rows, int cols, int row_mult, int row_off, hipStream_t s) {
+void launch_pack_rows(const void* src, void* dst, size_t rows, int cols, int row_mult, int row_off, int* err,
+                      hipStream_t s) {
   const size_t n = rows * (size_t)cols;
   if (n == 0) return;
   const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 16384);  // grid-stride beyond 4M elements
-  launch_k(pack_rows_kernel, blocks, 256, 0, s, (const bf16_t*)src, (f16_t*)dst, rows, cols, row_mult, row_off);
+  launch_k(pack_rows_kernel, blocks, 256, 0, s, (const bf16_t*)src, (f16_t*)dst, rows, cols, row_mult, row_off,
+           err);
 }
 
 // Gather of whole rows (the last row of each sequence of a batched prefill).
@@ -176,6 +198,29 @@ __global__ void gather_rows_kernel(const float* __restrict__ src, const int* __r
 void launch_gather_rows(const float* src, const int* idx, int n, int dim, float* dst, hipStream_t s) {
   if (n <= 0) return;
   launch_k(gather_rows_kernel, n, 256, 0, s, src, idx, dim, dst);
+}
+
+// Batched-prefill metadata from the kernel arguments: workgroup b writes the positions and
+// slot of sequence first + b's rows, its last row index and its descriptor.
+__global__ void __launch_bounds__(256) seq_meta_kernel(SeqMetaChunk c, int* __restrict__ row_pos,
+                                                       int* __restrict__ row_slot, int* __restrict__ last_idx,
+                                                       SeqDesc* __restrict__ table) {
+  const int b = blockIdx.x;
+  const SeqDesc sd = c.d[b];
+  for (int i = threadIdx.x; i < sd.n; i += blockDim.x) {
+    row_pos[sd.row0 + i] = sd.start + i;
+    row_slot[sd.row0 + i] = sd.slot;
+  }
+  if (threadIdx.x == 0) {
+    last_idx[c.first + b] = sd.row0 + sd.n - 1;
+    table[c.first + b] = sd;
+  }
+}
+
+void launch_seq_meta(const SeqMetaChunk& c, int* row_pos, int* row_slot, int* last_idx, SeqDesc* table,
+                     hipStream_t s) {
+  if (c.count <= 0) return;
+  launch_k(seq_meta_kernel, c.count, 256, 0, s, c, row_pos, row_slot, last_idx, table);
 }
 
 __global__ void fill_i32_kernel(int* p, int v, size_t n) {

@@ -23,6 +23,10 @@ __device__ __forceinline__ bool epi_row(const EpiParams& p, int m, int& pos, int
 // The inputs that do not depend on v (row position and slot, the rotation's cos
 // and sin) are gathered by qkv_prepare, so a kernel can fetch them while its dot
 // products are still in flight; qkv_store then writes the element.
+//
+// The storing helpers below return true when a value written in fp16 left fp16's
+// finite range; the kernel ORs these and raises LLM_DEVERR_RANGE once
+// (raise_range_error).
 struct QkvPrep {
   int pos, slot;
   float c, s;
@@ -46,8 +50,8 @@ __device__ __forceinline__ QkvPrep qkv_prepare(const EpiParams& p, int m, int n)
 }
 
 template <typename TA>
-__device__ __forceinline__ void qkv_store(const EpiParams& p, const QkvPrep& q, int m, int n, float v, float vp) {
-  if (!q.ok) return;
+__device__ __forceinline__ bool qkv_store(const EpiParams& p, const QkvPrep& q, int m, int n, float v, float vp) {
+  if (!q.ok) return false;
   const int d = p.head_dim;
   const int qd = p.n_heads * d, kd = p.n_kv_heads * d;
   if (n < qd + kd) {
@@ -61,25 +65,31 @@ __device__ __forceinline__ void qkv_store(const EpiParams& p, const QkvPrep& q, 
       size_t off = (((size_t)q.slot * p.n_kv_heads + g) * p.max_seq + q.pos) * d + e;
       reinterpret_cast<TA*>(p.k_cache)[off] = from_f32<TA>(r);
     }
-  } else {
-    const int col = n - qd - kd;
-    const int g = col / d, e = col % d;
-    size_t off = (((size_t)q.slot * p.n_kv_heads + g) * p.max_seq + q.pos) * d + e;
-    reinterpret_cast<TA*>(p.v_cache)[off] = from_f32<TA>(v);
+    return store_out_of_range<TA>(r);
   }
+  const int col = n - qd - kd;
+  const int g = col / d, e = col % d;
+  size_t off = (((size_t)q.slot * p.n_kv_heads + g) * p.max_seq + q.pos) * d + e;
+  reinterpret_cast<TA*>(p.v_cache)[off] = from_f32<TA>(v);
+  return store_out_of_range<TA>(v);
 }
 
 template <typename TA>
-__device__ __forceinline__ void epi_qkv(const EpiParams& p, int m, int n, float v, float vp) {
-  qkv_store<TA>(p, qkv_prepare(p, m, n), m, n, v, vp);
+__device__ __forceinline__ bool epi_qkv(const EpiParams& p, int m, int n, float v, float vp) {
+  return qkv_store<TA>(p, qkv_prepare(p, m, n), m, n, v, vp);
+}
+
+// One flag write per thread that stored an out-of-range value.
+__device__ __forceinline__ void raise_range_error(const EpiParams& p, bool bad) {
+  if (bad) atomicOr(p.err, LLM_DEVERR_RANGE_BIT);
 }
 
 // Four consecutive columns n .. n + 3 of one row (n % 4 == 0, head_dim % 4 == 0): they share
 // the role (q, k or v), head and row, hold RoPE pairs (n, n + 1) and (n + 2, n + 3), and land
 // in 4 consecutive fp16 elements of the destination, written as one 8-byte store.
-__device__ __forceinline__ void qkv_store4(const EpiParams& p, int m, int n, const float (&a)[4]) {
+__device__ __forceinline__ bool qkv_store4(const EpiParams& p, int m, int n, const float (&a)[4]) {
   int pos, slot;
-  if (!epi_row(p, m, pos, slot)) return;
+  if (!epi_row(p, m, pos, slot)) return false;
   const int d = p.head_dim;
   const int qd = p.n_heads * d, kd = p.n_kv_heads * d;
   const int kind = n < qd ? 0 : (n < qd + kd ? 1 : 2);
@@ -104,6 +114,7 @@ __device__ __forceinline__ void qkv_store4(const EpiParams& p, int m, int n, con
   hi.x = (f16_t)r[2];
   hi.y = (f16_t)r[3];
   *reinterpret_cast<uint2*>(dst) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  return f16_out_of_range(r[0]) | f16_out_of_range(r[1]) | f16_out_of_range(r[2]) | f16_out_of_range(r[3]);
 }
 
 // q|k|v epilogue of an MFMA tile held as acc[FM][FN] (16 x 16 blocks; this lane holds rows
@@ -111,19 +122,20 @@ __device__ __forceinline__ void qkv_store4(const EpiParams& p, int m, int n, con
 // head, RoPE pair, destination base and row stride depend only on the column, so they are
 // decoded once per block column; the rotation is written without branches (sign of the
 // partner term from the column parity; cos 1 and sin 0 for v columns).  All lanes must
-// call it (the RoPE partner comes from lane ^ 1).
+// call it (the RoPE partner comes from lane ^ 1).  Returns whether a stored value left fp16's range.
 //
 // STAGED: the rows are a prefill run (positions pos0 + m, slot slot0, ranges checked by the
 // caller) and the tile's rows of the RoPE table are staged in s_cos / s_sin (row m at
 // (m - m_tile) * d/2).  Otherwise each element validates its row (decode rows carry their
 // own position and slot) and reads the global table.
 template <int FM, int FN, bool STAGED>
-__device__ __forceinline__ void qkv_tile_epilogue(const EpiParams& p, const f32x4_t (&acc)[FM][FN], int M, int N,
+__device__ __forceinline__ bool qkv_tile_epilogue(const EpiParams& p, const f32x4_t (&acc)[FM][FN], int M, int N,
                                                   int m_base, int n_base, int lg, int l16,
                                                   const float* s_cos = nullptr, const float* s_sin = nullptr,
                                                   int m_tile = 0) {
   const int d = p.head_dim, half = d >> 1;
   const int qd = p.n_heads * d, kd = p.n_kv_heads * d;
+  bool bad = false;
 #pragma unroll
   for (int jn = 0; jn < FN; ++jn) {
     const int n = n_base + jn * 16 + l16;
@@ -150,7 +162,9 @@ __device__ __forceinline__ void qkv_tile_epilogue(const EpiParams& p, const f32x
             const int t = (m - m_tile) * half + j;
             const float c = rot ? s_cos[t] : 1.f;
             const float sn = rot ? s_sin[t] : 0.f;
-            dst[(size_t)m * rstride] = (f16_t)fmaf(sgn * vp, sn, v * c);
+            const float o = fmaf(sgn * vp, sn, v * c);
+            bad |= f16_out_of_range(o);
+            dst[(size_t)m * rstride] = (f16_t)o;
           }
         }
       }
@@ -166,7 +180,9 @@ __device__ __forceinline__ void qkv_tile_epilogue(const EpiParams& p, const f32x
           if (m < M && n < N && epi_row(p, m, pos, slot)) {
             const float c = rot ? p.rope_cos[(size_t)pos * half + j] : 1.f;
             const float sn = rot ? p.rope_sin[(size_t)pos * half + j] : 0.f;
-            const f16_t out = (f16_t)fmaf(sgn * vp, sn, v * c);
+            const float o = fmaf(sgn * vp, sn, v * c);
+            bad |= f16_out_of_range(o);
+            const f16_t out = (f16_t)o;
             if (kind == 0) reinterpret_cast<f16_t*>(p.out_act)[(size_t)m * p.ld + n] = out;
             else cache[(((size_t)slot * p.n_kv_heads + g) * p.max_seq + pos) * d + e] = out;
           }
@@ -174,6 +190,7 @@ __device__ __forceinline__ void qkv_tile_epilogue(const EpiParams& p, const f32x
       }
     }
   }
+  return bad;
 }
 
 // Residual add of an MFMA tile (layout as in qkv_tile_epilogue): all residual values are
@@ -204,10 +221,12 @@ __device__ __forceinline__ void resid_tile_epilogue(float* out, int ld, f32x4_t 
 
 // SwiGLU of one output column c from its gate (w1) and up (w3) values.
 template <typename TA>
-__device__ __forceinline__ void epi_swiglu(const EpiParams& p, int m, int c, float gate, float up) {
+__device__ __forceinline__ bool epi_swiglu(const EpiParams& p, int m, int c, float gate, float up) {
   const float LOG2E = 1.4426950408889634f;
   const float sg = gate * __builtin_amdgcn_rcpf(1.0f + exp2f(-gate * LOG2E));
-  reinterpret_cast<TA*>(p.out_act)[(size_t)m * p.ld + c] = from_f32<TA>(sg * up);
+  const float u = sg * up;
+  reinterpret_cast<TA*>(p.out_act)[(size_t)m * p.ld + c] = from_f32<TA>(u);
+  return store_out_of_range<TA>(u);
 }
 
 }  // namespace llm

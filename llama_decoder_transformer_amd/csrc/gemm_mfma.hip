@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
 
   // Epilogue.  A split-K workgroup stores its partial sums to slice blockIdx.y.
   if constexpr (EPI == EPI_QKV) {
-    qkv_tile_epilogue<FM, FN, false>(ep, acc, M, N, tm + wm * WM, tn + wn * WN, lg, l16);
+    raise_range_error(ep, qkv_tile_epilogue<FM, FN, false>(ep, acc, M, N, tm + wm * WM, tn + wn * WN, lg, l16));
     return;
   }
   float* const out_f32 = ep.out_f32 + (size_t)blockIdx.y * M * ep.ld;
@@ -170,6 +170,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
     resid_tile_epilogue<FM, FN>(out_f32, ep.ld, acc, M, N, tm + wm * WM, tn + wn * WN, lg, l16);
     return;
   }
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -181,7 +182,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
         const float v = acc[i][jn][r];
         if (EPI == EPI_SWIGLU) {
           const float vp = lane_xor1(v);
-          if (m < M && n < N && (n & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
+          if (m < M && n < N && (n & 1) == 0) bad |= epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
         } else if (m < M && n < N) {
           if (EPI == EPI_STORE_F32) out_f32[(size_t)m * ep.ld + n] = v;
           else out_f32[(size_t)m * ep.ld + n] += v;
@@ -189,6 +190,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_f16_kernel(const f16_t* _
       }
     }
   }
+  raise_range_error(ep, bad);
 }
 
 // ------------------------------------------------------------------ LDS-DMA variant
@@ -270,13 +272,14 @@ __device__ __forceinline__ void dma_tile_epilogue(const EpiParams& ep, f32x4_t (
       s_sin[idx] = ep.rope_sin[src];
     }
     __syncthreads();
-    qkv_tile_epilogue<FM, FN, true>(ep, acc, M, N, m0, n0, lg, l16, s_cos, s_sin, tm);
+    raise_range_error(ep, qkv_tile_epilogue<FM, FN, true>(ep, acc, M, N, m0, n0, lg, l16, s_cos, s_sin, tm));
     return;
   }
   if constexpr (EPI == EPI_RESID) {
     resid_tile_epilogue<FM, FN>(ep.out_f32, ep.ld, acc, M, N, m0, n0, lg, l16);
     return;
   }
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -288,7 +291,7 @@ __device__ __forceinline__ void dma_tile_epilogue(const EpiParams& ep, f32x4_t (
         const float v = acc[i][jn][r];
         if (EPI == EPI_SWIGLU) {
           const float vp = lane_xor1(v);
-          if (m < M && n < N && (n & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
+          if (m < M && n < N && (n & 1) == 0) bad |= epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
         } else if (m < M && n < N) {
           if (EPI == EPI_STORE_F32) ep.out_f32[(size_t)blockIdx.y * M * ep.ld + (size_t)m * ep.ld + n] = v;
           else ep.out_f32[(size_t)m * ep.ld + n] += v;
@@ -296,6 +299,7 @@ __device__ __forceinline__ void dma_tile_epilogue(const EpiParams& ep, f32x4_t (
       }
     }
   }
+  raise_range_error(ep, bad);
 }
 
 template <int BM, int BN, int WGM, int WGN, int NS, int EPI, bool SCHED>
@@ -793,19 +797,19 @@ static void gemm_init_attributes() {
 // The epilogue of four consecutive columns n .. n+3 of row m (N % 4 == 0 on the paths that use
 // it), so RoPE partners (2j, 2j+1) and SwiGLU gate/up pairs (2c, 2c+1) are together.
 // STORE_F32 writes to `out` (a split's slice of the partial sums, or the output).
+// Returns whether an fp16 value it stored left fp16's range.
 template <int EPI>
-__device__ __forceinline__ void epi_apply4(const EpiParams& ep, float* out, int m, int n, const float (&a)[4]) {
-  if (EPI == EPI_QKV && (ep.head_dim & 3) == 0) {
-    qkv_store4(ep, m, n, a);
-    return;
-  }
+__device__ __forceinline__ bool epi_apply4(const EpiParams& ep, float* out, int m, int n, const float (&a)[4]) {
+  if (EPI == EPI_QKV && (ep.head_dim & 3) == 0) return qkv_store4(ep, m, n, a);
+  bool bad = false;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     if (EPI == EPI_STORE_F32) out[(size_t)m * ep.ld + n + c] = a[c];
     else if (EPI == EPI_RESID) ep.out_f32[(size_t)m * ep.ld + n + c] += a[c];
-    else if (EPI == EPI_QKV) epi_qkv<f16_t>(ep, m, n + c, a[c], a[c ^ 1]);
-    else if (EPI == EPI_SWIGLU && (c & 1) == 0) epi_swiglu<f16_t>(ep, m, (n + c) >> 1, a[c], a[c + 1]);
+    else if (EPI == EPI_QKV) bad |= epi_qkv<f16_t>(ep, m, n + c, a[c], a[c ^ 1]);
+    else if (EPI == EPI_SWIGLU && (c & 1) == 0) bad |= epi_swiglu<f16_t>(ep, m, (n + c) >> 1, a[c], a[c + 1]);
   }
+  return bad;
 }
 
 // Split-K second pass: out = epilogue(sum over the splits of part[s][m][n]), summed in split
@@ -824,7 +828,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
   }
   const float a[4] = {v.x, v.y, v.z, v.w};
-  epi_apply4<EPI>(ep, ep.out_f32, m, n, a);
+  raise_range_error(ep, epi_apply4<EPI>(ep, ep.out_f32, m, n, a));
 }
 
 // Split-K reduction of a residual projection fused with the RMSNorm that consumes its result:
@@ -836,7 +840,7 @@ template <int V4>
 __global__ void __launch_bounds__(1024) splitk_resid_norm_kernel(const float* __restrict__ part, int splits, int M,
                                                                  int N, float* __restrict__ x, int ldx,
                                                                  const float* __restrict__ w, float eps,
-                                                                 f16_t* __restrict__ a) {
+                                                                 f16_t* __restrict__ a, int* err) {
   __shared__ float red[16];
   const int m = blockIdx.x;
   const size_t slice = (size_t)M * N;
@@ -867,15 +871,21 @@ __global__ void __launch_bounds__(1024) splitk_resid_norm_kernel(const float* __
   for (int i = 0; i < 16; ++i) tot += red[i];
   const float inv = 1.0f / sqrtf(tot / (float)N + eps);
   f16_t* ar = a + (size_t)m * N;
+  bool bad = false;
 #pragma unroll
   for (int j = 0; j < V4; ++j) {
     const int i = (threadIdx.x + 1024 * j) * 4;
     if (i < N) {
       const f32x4_t g = *reinterpret_cast<const f32x4_t*>(w + i);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) ar[i + k] = from_f32<f16_t>(v[j][k] * inv * g[k]);
+      for (int k = 0; k < 4; ++k) {
+        const float y = v[j][k] * inv * g[k];
+        bad |= f16_out_of_range(y);
+        ar[i + k] = from_f32<f16_t>(y);
+      }
     }
   }
+  if (bad) atomicOr(err, LLM_DEVERR_RANGE_BIT);
 }
 
 // Weight-streaming GEMM for batches of at most 64 rows (batched decode).  Such a projection is
@@ -983,6 +993,7 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(const f16_t* __restric
       for (int r = 0; r < 4; ++r) red[(wid * BM + i * 16 + lg * 4 + r) * BN + jn * 16 + l16] = acc[i][jn][r];
   __syncthreads();
   float* out = EPI == EPI_STORE_F32 ? ep.out_f32 + (size_t)blockIdx.y * M * ep.ld : ep.out_f32;
+  bool bad = false;
   for (int g = tid; g < BM * BN / 4; g += 256) {
     const int m = g / (BN / 4), c4 = (g % (BN / 4)) * 4;
     if (m >= M || tn + c4 >= N) continue;
@@ -993,8 +1004,9 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(const f16_t* __restric
       v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
     }
     const float a[4] = {v.x, v.y, v.z, v.w};
-    epi_apply4<EPI>(ep, out, m, tn + c4, a);
+    bad |= epi_apply4<EPI>(ep, out, m, tn + c4, a);
   }
+  raise_range_error(ep, bad);
 }
 
 // Launch over N / (16 FN) tiles and `splits` K slices (whole stages of ST_BK each); returns the
@@ -1284,9 +1296,11 @@ bool launch_gemm_f16_resid_norm(const void* A, const void* W, int M, int N, int 
   const int ns = gemm_stream_run(st, (const f16_t*)A, (const f16_t*)W, M, N, K, pe, s);
   f16_t* a = (f16_t*)a_out;
   if (N <= 4096)
-    launch_k(splitk_resid_norm_kernel<1>, M, 1024, 0, s, splitk_ws, ns, M, N, ep.out_f32, ep.ld, norm_w, eps, a);
+    launch_k(splitk_resid_norm_kernel<1>, M, 1024, 0, s, splitk_ws, ns, M, N, ep.out_f32, ep.ld, norm_w, eps, a,
+             ep.err);
   else
-    launch_k(splitk_resid_norm_kernel<2>, M, 1024, 0, s, splitk_ws, ns, M, N, ep.out_f32, ep.ld, norm_w, eps, a);
+    launch_k(splitk_resid_norm_kernel<2>, M, 1024, 0, s, splitk_ws, ns, M, N, ep.out_f32, ep.ld, norm_w, eps, a,
+             ep.err);
   return true;
 }
 

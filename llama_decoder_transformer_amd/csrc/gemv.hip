@@ -9,10 +9,12 @@
 // epilogue (RoPE / cache write, SwiGLU, residual add, fp32 store) runs on the
 // R * MR finished values.
 //
-// With NORM the input is the fp32 residual stream x and the RMSNorm is fused:
-// the block accumulates sum_k W[n][k] * (x[k] * g[k]) and sum_k x[k]^2 in the
-// same pass and scales by 1 / sqrt(mean(x^2) + eps) at the end (the "rms_norm"
-// of the "Building llama3 from scratch" page, distributed over the dot product).
+// With NORM the input is the fp32 residual stream x and the RMSNorm is fused (the
+// "rms_norm" of the "Building llama3 from scratch" page): the fp32 kernel accumulates
+// sum_k W[n][k] * (x[k] * g[k]) and sum_k x[k]^2 in the same pass and scales by
+// 1 / sqrt(mean(x^2) + eps) at the end; the fp16 kernel first takes sum_k x[k]^2 of
+// its rows and then multiplies by the normalised activations, rounded to fp16 as the
+// separate RMSNorm kernel rounds them.
 #include "common.h"
 #include "epilogue.h"
 #include "launch.h"
@@ -130,9 +132,14 @@ __global__ void __launch_bounds__(256) gemv_kernel(const void* __restrict__ Ain,
 // fp16 weights (the bf16-weight path): the same scheme with the weights kept as
 // raw 16-byte words until use, so two chunks x R rows of loads (2R per lane) are
 // issued before any math.  The products use the packed fp16 dot instruction (two
-// products per lane per instruction, fp32 accumulation): fp16 activations are
-// used as loaded, and with the fused norm x * g is rounded to fp16 once, as the
-// separate RMSNorm of the matrix-core path rounds its output.
+// products per lane per instruction, fp32 accumulation) on fp16 activations.
+//
+// With the fused norm, the block first sums x^2 over its rows (fp32, through LDS),
+// with the first chunks' weight loads already in flight, and the loop then uses
+// fp16(x * inv_rms * g): the value the separate RMSNorm kernel of the matrix-core
+// path stores, so both paths see the same normalised activations and a large
+// residual cannot overflow fp16 before it is scaled down.  A normalised value
+// outside fp16's range raises LLM_DEVERR_RANGE.
 
 template <int MR, int R, int EPI, bool NORM>
 __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ain, const f16_t* __restrict__ W,
@@ -164,20 +171,17 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   for (int r = 0; r < R; ++r) wr[r] = W + (size_t)min(n0 + r, N - 1) * K;
 
   float acc[MR][R];
-  float ss[MR];
 #pragma unroll
-  for (int i = 0; i < MR; ++i) {
-    ss[i] = 0.f;
+  for (int i = 0; i < MR; ++i)
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[i][r] = 0.f;
-  }
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
   const int nchunks = (K + KW - 1) / KW;
-  for (int c0 = wid; c0 < nchunks; c0 += 8) {
-    int kk[2];
-    bool ok[2];
-    u32x4_t wraw[2][R];
+  int kk[2];
+  bool ok[2];
+  u32x4_t wraw[2][R];
+  auto load_w = [&](int c0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       kk[u] = (c0 + 4 * u) * KW + lane * 8;
@@ -186,6 +190,40 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
       for (int r = 0; r < R; ++r)
         wraw[u][r] = ok[u] ? *reinterpret_cast<const u32x4_t*>(wr[r] + kk[u]) : zero;
     }
+  };
+  // The first iteration's weight loads go out before the norm statistics.
+  if (wid < nchunks) load_w(wid);
+
+  float inv[MR];
+  bool range_bad = false;
+  if (NORM) {
+    float ss[MR];
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      ss[i] = 0.f;
+      if (i < mrows) {
+        const float* xr = reinterpret_cast<const float*>(Ain) + (size_t)(m0 + i) * K;
+        for (int k = (wid * WAVE + lane) * 4; k < K; k += 256 * 4) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(xr + k);
+          ss[i] += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        }
+      }
+      ss[i] = wave_sum(ss[i]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < MR; ++i) s_ss[wid][i] = ss[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      const float tot = s_ss[0][i] + s_ss[1][i] + s_ss[2][i] + s_ss[3][i];
+      inv[i] = 1.0f / sqrtf(tot / (float)K + eps);
+    }
+  }
+
+  for (int c0 = wid; c0 < nchunks; c0 += 8) {
+    if (c0 != wid) load_w(c0);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if (!ok[u]) continue;
@@ -200,9 +238,12 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
             float a[8];
             load8(reinterpret_cast<const float*>(Ain) + (size_t)(m0 + i) * K + kk[u], a);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ss[i] = fmaf(a[e], a[e], ss[i]);
+            for (int e = 0; e < 8; ++e) {
+              a[e] = a[e] * inv[i] * g[e];
+              range_bad |= f16_out_of_range(a[e]);
+            }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ah[e] = pack_h2(a[2 * e] * g[2 * e], a[2 * e + 1] * g[2 * e + 1]);
+            for (int e = 0; e < 4; ++e) ah[e] = pack_h2(a[2 * e], a[2 * e + 1]);
           } else {
             const u32x4_t raw =
                 *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const f16_t*>(Ain) + (size_t)(m0 + i) * K + kk[u]);
@@ -227,14 +268,12 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   for (int i = 0; i < MR; ++i) {
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[i][r] = wave_sum(acc[i][r]);
-    if (NORM) ss[i] = wave_sum(ss[i]);
   }
   if (lane == 0) {
 #pragma unroll
     for (int i = 0; i < MR; ++i) {
 #pragma unroll
       for (int r = 0; r < R; ++r) s_acc[wid][i][r] = acc[i][r];
-      s_ss[wid][i] = ss[i];
     }
   }
   __syncthreads();
@@ -242,24 +281,19 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   if (ethread) {
     const int i = ei, r = er;
     const int m = m0 + i, n = n0 + r;
-    float v = s_acc[0][i][r] + s_acc[1][i][r] + s_acc[2][i][r] + s_acc[3][i][r];
-    float vp = s_acc[0][i][r ^ 1] + s_acc[1][i][r ^ 1] + s_acc[2][i][r ^ 1] + s_acc[3][i][r ^ 1];
-    if (NORM) {
-      const float tot = s_ss[0][i] + s_ss[1][i] + s_ss[2][i] + s_ss[3][i];
-      const float inv = 1.0f / sqrtf(tot / (float)K + eps);
-      v *= inv;
-      vp *= inv;
-    }
+    const float v = s_acc[0][i][r] + s_acc[1][i][r] + s_acc[2][i][r] + s_acc[3][i][r];
+    const float vp = s_acc[0][i][r ^ 1] + s_acc[1][i][r ^ 1] + s_acc[2][i][r ^ 1] + s_acc[3][i][r ^ 1];
     if (EPI == EPI_STORE_F32) {
       ep.out_f32[(size_t)m * ep.ld + n] = v;
     } else if (EPI == EPI_RESID) {
       ep.out_f32[(size_t)m * ep.ld + n] = e_resid + v;
     } else if (EPI == EPI_QKV) {
-      qkv_store<f16_t>(ep, e_qkv, m, n, v, vp);
+      range_bad |= qkv_store<f16_t>(ep, e_qkv, m, n, v, vp);
     } else if (EPI == EPI_SWIGLU) {
-      if ((r & 1) == 0) epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
+      if ((r & 1) == 0) range_bad |= epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
     }
   }
+  raise_range_error(ep, range_bad);
 }
 
 template <int MR, int R, bool NORM>

@@ -56,14 +56,16 @@ struct EpiParams {
 // Embedding gather: x[m][:] = float(E[tok[m]][:]).
 void launch_embed(int dtype, const void* emb, const int* tokens, int M, int dim, int vocab, float* x,
                   int* err, hipStream_t s);
-// RMSNorm of fp32 rows into the activation dtype.
-void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, float eps, void* out,
+// RMSNorm of fp32 rows into the activation dtype (an fp16 result out of range sets err bit 8).
+void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, float eps, void* out, int* err,
                     hipStream_t s);
 // Widen a [n] vector of the storage dtype to fp32.
 void launch_to_f32(int dtype, const void* src, float* dst, size_t n, hipStream_t s);
 void launch_fill_i32(int* p, int v, size_t n, hipStream_t s);
-// bf16 [rows][cols] -> fp16 rows placed at dst row r * row_mult + row_off.
-void launch_pack_rows(const void* src, void* dst, size_t rows, int cols, int row_mult, int row_off, hipStream_t s);
+// bf16 [rows][cols] -> fp16 rows placed at dst row r * row_mult + row_off (a weight outside fp16's
+// range sets err bit 8).
+void launch_pack_rows(const void* src, void* dst, size_t rows, int cols, int row_mult, int row_off, int* err,
+                      hipStream_t s);
 // dst[i][:] = src[idx[i]][:] for i < n (rows of `dim` floats).
 void launch_gather_rows(const float* src, const int* idx, int n, int dim, float* dst, hipStream_t s);
 // Greedy argmax per row (two passes through `partial`, >= rows*argmax_blocks(vocab)*2 words).
@@ -110,5 +112,30 @@ bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads);
 void launch_attn_prefill(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0,
                          int n_tokens, int n_heads, int n_kv_heads, int head_dim, int max_seq,
                          void* out, hipStream_t s);
+
+// One sequence of a batched prefill: its rows [row0, row0 + n) of the activations, positions
+// start .. start + n - 1 of cache slot `slot`, and the index of its first query block in the
+// batched prefill attention's grid (blocks of attn_prefill_block_rows queries).
+struct SeqDesc {
+  int row0, n, start, slot, blk0, pad[3];
+};
+// Query rows per workgroup of the prefill attention for sequences of at most max_n tokens.
+int attn_prefill_block_rows(int max_n, int n_heads, int n_kv_heads);
+// Prefill attention of several sequences in one launch over (sequence, query block) work items:
+// seqs (device, nseq entries, blk0 ascending from 0) as above, n_blocks = sum of the sequences'
+// query blocks, max_n = the longest sequence (it sets the block size).
+void launch_attn_prefill_varlen(const void* q, const void* k_cache, const void* v_cache, const SeqDesc* seqs,
+                                int nseq, int n_blocks, int max_n, int n_heads, int n_kv_heads, int head_dim,
+                                int max_seq, void* out, hipStream_t s);
+// Per-row positions and slots, last-row indices and the device copy of up to SEQ_META_CHUNK
+// sequence descriptors, taken from the kernel arguments (no host staging buffer): entries
+// first .. first + count - 1 of the batch.
+constexpr int SEQ_META_CHUNK = 32;
+struct SeqMetaChunk {
+  int first, count, pad[2];
+  SeqDesc d[SEQ_META_CHUNK];
+};
+void launch_seq_meta(const SeqMetaChunk& c, int* row_pos, int* row_slot, int* last_idx, SeqDesc* table,
+                     hipStream_t s);
 
 }  // namespace llm

@@ -85,7 +85,7 @@ struct PackedLayout {
 
 // Workspace layout.
 struct WorkLayout {
-  size_t flags, x, a, q, o, u, attn, amax, splitk, splitk_floats, rowmeta, last, total;
+  size_t flags, x, a, q, o, u, attn, amax, splitk, splitk_floats, rowmeta, seqtab, last, total;
   explicit WorkLayout(const llm_config& c) {
     Dims d(c);
     const size_t R = (size_t)d.rows();
@@ -108,8 +108,10 @@ struct WorkLayout {
         for (auto& sh : shapes) splitk_floats = std::max(splitk_floats, gemm_splitk_floats(M, sh[0], sh[1]));
     }
     splitk = p; p = align256(p + splitk_floats * 4);
-    // batched prefill: per-row position and slot, per-sequence last row, gathered last rows
+    // batched prefill: per-row position and slot, per-sequence last row, sequence descriptors,
+    // gathered last rows
     rowmeta = p; p = align256(p + (2 * R + (size_t)d.B) * 4);
+    seqtab = p; p = align256(p + (size_t)d.B * sizeof(SeqDesc));
     last = p; p = align256(p + (size_t)d.B * d.dim * 4);
     total = p;
   }
@@ -161,10 +163,8 @@ struct llm_model {
   float* splitk;
   size_t splitk_floats;
   int* rowmeta;          // device: [R] positions, [R] slots, [B] last-row indices (batched prefill)
+  SeqDesc* seqtab;       // device: [B] sequence descriptors (batched prefill)
   float* last;           // device: [B][dim] gathered last rows (batched prefill)
-  int* meta_host;        // pinned host staging for rowmeta
-  hipEvent_t meta_ev;    // recorded after the staging copy; waited on before the buffer is refilled
-  bool meta_pending;
   bool mfma_prefill;
   hipStream_t cap_stream;
   std::vector<GraphEntry> graphs;
@@ -174,6 +174,7 @@ struct llm_model {
   std::vector<Bracket> pending;
   std::vector<hipEvent_t> event_pool;
   int64_t t_launches[LLM_K_COUNT] = {};
+  int64_t t_kernels[LLM_K_COUNT] = {};
   double t_ms[LLM_K_COUNT] = {};
 };
 
@@ -212,7 +213,10 @@ struct ModelTimer final : LaunchTimer {
     }
     return true;
   }
-  void done(hipEvent_t a, hipEvent_t b) override { m->pending.push_back({kind, a, b}); }
+  void done(hipEvent_t a, hipEvent_t b) override {
+    m->pending.push_back({kind, a, b});
+    m->t_kernels[kind] += 1;
+  }
 };
 
 struct Timed {
@@ -277,7 +281,7 @@ void project(llm_model* m, const void* A, const void* W, int M, int N, int K, co
   const llm_config& c = m->cfg;
   if (use_mfma(m, M)) {
     if (norm_w) {
-      launch_rmsnorm(c.dtype, (const float*)A, norm_w, M, K, c.norm_eps, m->a, s);
+      launch_rmsnorm(c.dtype, (const float*)A, norm_w, M, K, c.norm_eps, m->a, m->flags, s);
       A = m->a;
     }
     launch_gemm_f16(A, W, M, N, K, ep, m->splitk, m->splitk_floats, s);
@@ -286,21 +290,22 @@ void project(llm_model* m, const void* A, const void* W, int M, int N, int K, co
   }
 }
 
-// One sequence of a batched prefill: rows [row0, row0 + n) of the workspace, positions start..,
-// cache slot `slot`.
-struct SeqSpan {
-  int row0, n, start, slot;
+// The sequences of a batched prefill as the attention launch needs them: nseq descriptors on the
+// device, n_blocks query blocks in all, the longest sequence max_n.
+struct Varlen {
+  const SeqDesc* seqs;
+  int nseq, n_blocks, max_n;
 };
 
 // One decoder block on M rows of m->x.  Rows are either a prefill run
-// (row_pos == nullptr: positions pos0.., slot slot0), a batched prefill (`seqs`), or decode
-// rows with their own positions and slots.
+// (row_pos == nullptr: positions pos0.., slot slot0), a batched prefill (`vl`, with per-row
+// positions and slots in row_pos / row_slot), or decode rows with their own positions and slots.
 // a_ready: m->a already holds rmsnorm(x) with this layer's attention norm (left there by the
 // previous layer's down projection).  next_norm: the next layer's attention norm, or null.
 // Returns whether m->a now holds rmsnorm(x) with next_norm.  The two RMSNorms ahead of MFMA
 // projections ride in the split-K reduction of the wo / down projection when that is split.
 bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_slot, int pos0, int slot0,
-               bool prefill, hipStream_t s, const std::vector<SeqSpan>* seqs = nullptr, bool a_ready = false,
+               bool prefill, hipStream_t s, const Varlen* vl = nullptr, bool a_ready = false,
                const float* next_norm = nullptr) {
   const llm_config& c = m->cfg;
   const LayerPtrs& L = m->layers[l];
@@ -326,11 +331,9 @@ bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
 
   {
     Timed t(m, LLM_K_ATTN, s);
-    if (prefill && m->mfma_prefill && seqs) {
-      const size_t rb = (size_t)H * hd * m->es;  // bytes of one q / o row
-      for (const SeqSpan& q : *seqs)
-        launch_attn_prefill((char*)m->q + q.row0 * rb, k_section(m, l), v_section(m, l), q.slot, q.start, q.n, H, G,
-                            hd, c.max_seq_len, (char*)m->o + q.row0 * rb, s);
+    if (prefill && m->mfma_prefill && vl) {
+      launch_attn_prefill_varlen(m->q, k_section(m, l), v_section(m, l), vl->seqs, vl->nseq, vl->n_blocks, vl->max_n,
+                                 H, G, hd, c.max_seq_len, m->o, s);
     } else if (prefill && m->mfma_prefill && !row_pos)
       launch_attn_prefill(m->q, k_section(m, l), v_section(m, l), slot0, pos0, M, H, G, hd, c.max_seq_len, m->o, s);
     else
@@ -377,11 +380,11 @@ bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
 // All layers over M rows, each passing its successor the attention-normed activations when its
 // down projection produced them.
 void run_layers(llm_model* m, int M, const int* row_pos, const int* row_slot, int pos0, int slot0, bool prefill,
-                hipStream_t s, const std::vector<SeqSpan>* seqs = nullptr) {
+                hipStream_t s, const Varlen* vl = nullptr) {
   const int n = m->cfg.n_layers;
   bool a_ready = false;
   for (int l = 0; l < n; ++l)
-    a_ready = run_layer(m, l, M, row_pos, row_slot, pos0, slot0, prefill, s, seqs, a_ready,
+    a_ready = run_layer(m, l, M, row_pos, row_slot, pos0, slot0, prefill, s, vl, a_ready,
                         l + 1 < n ? m->layers[l + 1].attn_norm : nullptr);
 }
 
@@ -487,10 +490,8 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   m->splitk = (float*)(ws + wl.splitk);
   m->splitk_floats = wl.splitk_floats;
   m->rowmeta = (int*)(ws + wl.rowmeta);
+  m->seqtab = (SeqDesc*)(ws + wl.seqtab);
   m->last = (float*)(ws + wl.last);
-  m->meta_host = nullptr;
-  m->meta_ev = nullptr;
-  m->meta_pending = false;
   m->mfma_prefill = c.dtype == LLM_BF16 && attn_prefill_supported(d.hd, d.H, d.G);
   m->cap_stream = nullptr;
 
@@ -498,12 +499,15 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   const size_t row = (size_t)d.dim * es;
   hipError_t e = hipSuccess;
   const bool h = c.dtype == LLM_BF16;
+  // The device error flags start cleared; weight packing may raise LLM_DEVERR_RANGE.
+  launch_fill_i32(m->flags, 0, 64, s);
   // Copy rows [0, rows) of src ([rows][cols]) to dst rows r * mult + off.  The fp32
-  // path copies as is; bf16 weights are stored as fp16 (exact conversion).
+  // path copies as is; bf16 weights are stored as fp16 (exact inside fp16's normal
+  // range; an out-of-range weight raises LLM_DEVERR_RANGE).
   auto put = [&](void* dst, const void* src, size_t rows, int cols, int mult, int off) {
     if (e != hipSuccess) return;
     if (h) {
-      launch_pack_rows(src, dst, rows, cols, mult, off, s);
+      launch_pack_rows(src, dst, rows, cols, mult, off, m->flags, s);
     } else if (mult == 1) {
       e = hipMemcpyAsync((char*)dst + (size_t)off * cols * 4, src, rows * cols * 4, hipMemcpyDeviceToDevice, s);
     } else {
@@ -548,13 +552,10 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   }
   if (e == hipSuccess) e = hipMemcpyAsync(m->rope_cos, hc.data(), hc.size() * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(m->rope_sin, hs.data(), hs.size() * 4, hipMemcpyHostToDevice, s);
-  launch_fill_i32(m->flags, 0, 64, s);
 
   if (e == hipSuccess) e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipHostMalloc((void**)&m->meta_host, (2 * (size_t)d.rows() + d.B) * sizeof(int));
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&m->meta_ev, hipEventDisableTiming);
   if (e != hipSuccess) {
     delete m;
     return fail(LLM_ERR_HIP, std::string("init: ") + hipGetErrorString(e));
@@ -589,9 +590,10 @@ llm_status llm_prefill_batch(llm_model* m, int32_t batch, const int32_t* slots_h
   const llm_config& c = m->cfg;
   if (batch < 1) return fail(LLM_ERR_INVALID_ARG, "batch must be >= 1");
   if (batch > c.max_batch) return fail(LLM_ERR_OUT_OF_RANGE, "batch > max_batch");
-  std::vector<SeqSpan> seqs((size_t)batch);
+  std::vector<SeqDesc> seqs((size_t)batch);
   std::vector<char> used((size_t)c.max_batch, 0);
   long long total = 0;
+  int max_n = 0;
   for (int b = 0; b < batch; ++b) {
     const int slot = slots_host[b], start = starts_host[b], n = lens_host[b];
     if (n < 1) return fail(LLM_ERR_INVALID_ARG, "every sequence needs >= 1 token");
@@ -600,37 +602,46 @@ llm_status llm_prefill_batch(llm_model* m, int32_t batch, const int32_t* slots_h
     used[slot] = 1;
     if (start < 0 || (long long)start + n > c.max_seq_len)
       return fail(LLM_ERR_OUT_OF_RANGE, "start + length > max_seq_len");
-    seqs[b] = SeqSpan{(int)total, n, start, slot};
+    if (total + n > c.max_prefill_tokens) return fail(LLM_ERR_OUT_OF_RANGE, "total tokens > max_prefill_tokens");
+    std::memset(&seqs[b], 0, sizeof(SeqDesc));
+    seqs[b].row0 = (int)total;
+    seqs[b].n = n;
+    seqs[b].start = start;
+    seqs[b].slot = slot;
     total += n;
+    max_n = std::max(max_n, n);
   }
-  if (total > c.max_prefill_tokens) return fail(LLM_ERR_OUT_OF_RANGE, "total tokens > max_prefill_tokens");
   const int T = (int)total;
-  const int R = std::max(c.max_prefill_tokens, c.max_batch);
-  hipStream_t s = as_stream(stream);
-  // Per-row positions and slots and the per-sequence last rows go to the device through the
-  // pinned staging buffer; the previous call's copy must have left it before it is refilled.
-  if (m->meta_pending && hipEventSynchronize(m->meta_ev) != hipSuccess) return hip_check("batched prefill staging");
-  int* hp = m->meta_host;
-  for (const SeqSpan& q : seqs)
-    for (int i = 0; i < q.n; ++i) {
-      hp[q.row0 + i] = q.start + i;
-      hp[R + q.row0 + i] = q.slot;
+  // Query blocks of each sequence in the one attention launch.
+  int n_blocks = 0;
+  if (m->mfma_prefill) {
+    const int qb = attn_prefill_block_rows(max_n, c.n_heads, c.n_kv_heads);
+    for (SeqDesc& q : seqs) {
+      q.blk0 = n_blocks;
+      n_blocks += (q.n + qb - 1) / qb;
     }
-  for (int b = 0; b < batch; ++b) hp[2 * R + b] = seqs[b].row0 + seqs[b].n - 1;
+  }
+  const int R = std::max(c.max_prefill_tokens, c.max_batch);
   int* row_pos = m->rowmeta;
   int* row_slot = m->rowmeta + R;
   int* last_idx = m->rowmeta + 2 * R;
-  hipError_t e = hipMemcpyAsync(row_pos, hp, (size_t)T * sizeof(int), hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(row_slot, hp + R, (size_t)T * sizeof(int), hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(last_idx, hp + 2 * R, (size_t)batch * sizeof(int), hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipEventRecord(m->meta_ev, s);
-  if (e != hipSuccess) return fail(LLM_ERR_HIP, std::string("batched prefill staging: ") + hipGetErrorString(e));
-  m->meta_pending = true;
+  hipStream_t s = as_stream(stream);
+  // The per-sequence descriptors travel in kernel arguments, which the launch copies: no host
+  // staging buffer, so nothing here waits for the device.
+  for (int b0 = 0; b0 < batch; b0 += SEQ_META_CHUNK) {
+    SeqMetaChunk ch;
+    std::memset(&ch, 0, sizeof(ch));
+    ch.first = b0;
+    ch.count = std::min(SEQ_META_CHUNK, batch - b0);
+    for (int i = 0; i < ch.count; ++i) ch.d[i] = seqs[b0 + i];
+    launch_seq_meta(ch, row_pos, row_slot, last_idx, m->seqtab, s);
+  }
   {
     Timed t(m, LLM_K_EMBED, s);
     launch_embed(c.dtype, m->emb, tokens_dev, T, c.dim, c.vocab_size, m->x, m->flags, s);
   }
-  run_layers(m, T, row_pos, row_slot, 0, 0, true, s, &seqs);
+  const Varlen vl{m->seqtab, batch, n_blocks, max_n};
+  run_layers(m, T, row_pos, row_slot, 0, 0, true, s, &vl);
   launch_gather_rows(m->x, last_idx, batch, c.dim, m->last, s);
   lm_head(m, m->last, batch, logits_dev, s);
   return hip_check("batched prefill launch");
@@ -745,15 +756,16 @@ llm_status llm_set_kernel_timing(llm_model* m, int32_t enable) {
   if (!m) return fail(LLM_ERR_INVALID_ARG, "NULL model");
   if (resolve_timing(m) != LLM_OK) return fail(LLM_ERR_HIP, "timing events failed");
   m->timing = enable != 0;
-  for (int k = 0; k < LLM_K_COUNT; ++k) { m->t_launches[k] = 0; m->t_ms[k] = 0.0; }
+  for (int k = 0; k < LLM_K_COUNT; ++k) { m->t_launches[k] = 0; m->t_kernels[k] = 0; m->t_ms[k] = 0.0; }
   return LLM_OK;
 }
 
-llm_status llm_kernel_timing(llm_model* m, int32_t kind, int64_t* launches, double* total_ms) {
+llm_status llm_kernel_timing(llm_model* m, int32_t kind, int64_t* launches, int64_t* kernels, double* total_ms) {
   if (!m || !launches || !total_ms) return fail(LLM_ERR_INVALID_ARG, "NULL model or output");
   if (kind < 0 || kind >= LLM_K_COUNT) return fail(LLM_ERR_INVALID_ARG, "unknown kernel group");
   if (resolve_timing(m) != LLM_OK) return fail(LLM_ERR_HIP, "timing events failed");
   *launches = m->t_launches[kind];
+  if (kernels) *kernels = m->t_kernels[kind];
   *total_ms = m->t_ms[kind];
   return LLM_OK;
 }
@@ -764,11 +776,6 @@ void llm_free(llm_model* m) {
   for (auto e : m->event_pool) (void)hipEventDestroy(e);
   for (auto& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
-  if (m->meta_ev) {
-    (void)hipEventSynchronize(m->meta_ev);
-    (void)hipEventDestroy(m->meta_ev);
-  }
-  if (m->meta_host) (void)hipHostFree(m->meta_host);
   delete m;
 }
 

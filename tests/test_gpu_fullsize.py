@@ -3,10 +3,7 @@
 * 32-layer model, prompt of 512 ids: prefill logits and the first decode steps
   (the GPU fed the oracle's greedy tokens) against the fp32-matmul oracle; the
   graph-replayed generation loop against direct decode steps.
-* Prefill of 8192 ids: the KV cache the GPU wrote for the first positions against
-  the oracle's prefix run (causality makes those entries independent of later
-  tokens), and the last-position logits against a prefill of 8191 ids plus one
-  decode step (cached decode equals recompute).
+* (The prefill of 8192 ids is in test_gpu_long_prefill.py.)
 * Batched decode, 64 sequences with cached lengths U{1024..8192} and N(0,1)
   caches: seeded rows (including the shortest and longest) against the oracle,
   and every row against a batch-1 decode of the same row.
@@ -109,35 +106,6 @@ def test_llama3_8b_prefill_512_and_decode_match_oracle(w8b):
     assert m.read_device_error() == 0
     del m
     _free()
-
-
-def test_llama3_8b_prefill_8192(w8b):
-    shape0, bits, oracle = w8b
-    wl = inputs.WORKLOADS["llama3-8b-long-prefill"]
-    shape = wl.shape
-    S = wl.prompt_len
-    prompt = inputs.token_ids(shape.vocab_size, S)
-    m = _gpu_model(shape, bits, 1, S)
-    full = m.prefill(_i32(prompt)).cpu().numpy()
-    assert np.all(np.isfinite(full))
-    kv = m.kv_cache_view()
-    Pfx = 48
-    gpu_k = kv[:, 0, 0, :, :Pfx].float().cpu().numpy()  # [L, G, Pfx, d]
-    gpu_v = kv[:, 1, 0, :, :Pfx].float().cpu().numpy()
-    # cached decode of the last token equals the full prefill's last-position logits
-    m.prefill(_i32(prompt[:-1]))
-    dec = m.decode_step(_i32([0]), _i32([S - 1]), _i32([prompt[-1]])).cpu().numpy()[0]
-    e_dec = rel_err(dec, full)
-    assert int(np.argmax(dec)) == int(np.argmax(full)) or near_tie_ok(int(np.argmax(dec)), full, TOL)
-    del m
-    _free()
-    om = oracle(Pfx)
-    cache = om.new_cache(Pfx)
-    om.prefill(prompt[:Pfx], cache=cache)
-    ek = max(rel_err(gpu_k[l].transpose(1, 0, 2), cache[l][0]) for l in range(shape.n_layers))
-    ev = max(rel_err(gpu_v[l].transpose(1, 0, 2), cache[l][1]) for l in range(shape.n_layers))
-    print(f"[8b prefill 8192] prefix K rel err {ek:.3e}, V rel err {ev:.3e}, decode-vs-prefill {e_dec:.3e}", flush=True)
-    assert ek <= TOL and ev <= TOL and e_dec <= TOL
 
 
 def _fill_cache(kv, shape, lengths, seed):
