@@ -136,10 +136,9 @@ __global__ void __launch_bounds__(256) gemv_kernel(const void* __restrict__ Ain,
 //
 // With the fused norm, the block first sums x^2 over its rows (fp32, through LDS),
 // with the first chunks' weight loads already in flight, and the loop then uses
-// fp16(x * inv_rms * g): the value the separate RMSNorm kernel of the matrix-core
-// path stores, so both paths see the same normalised activations and a large
-// residual cannot overflow fp16 before it is scaled down.  A normalised value
-// outside fp16's range raises LLM_DEVERR_RANGE.
+// fp16(x * inv_rms * g), as the separate RMSNorm kernel of the matrix-core path
+// rounds its output, so a large residual cannot overflow fp16 before it is scaled
+// down.  A normalised value outside fp16's range raises LLM_DEVERR_RANGE.
 
 template <int MR, int R, int EPI, bool NORM>
 __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ain, const f16_t* __restrict__ W,
@@ -175,24 +174,39 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   for (int i = 0; i < MR; ++i)
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[i][r] = 0.f;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-
   const int nchunks = (K + KW - 1) / KW;
   int kk[2];
   bool ok[2];
   u32x4_t wraw[2][R];
+  // Every load below is unconditional, from an address clamped into the row (K % 8 == 0), and
+  // a chunk past the row's end is skipped at use: with no load under a branch the compiler
+  // counts the loads in flight exactly and waits only for the ones it needs.
   auto load_w = [&](int c0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       kk[u] = (c0 + 4 * u) * KW + lane * 8;
       ok[u] = kk[u] < K;
+      const int kc = min(kk[u], K - 8);
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        wraw[u][r] = ok[u] ? *reinterpret_cast<const u32x4_t*>(wr[r] + kk[u]) : zero;
+      for (int r = 0; r < R; ++r) wraw[u][r] = *reinterpret_cast<const u32x4_t*>(wr[r] + kc);
     }
   };
-  // The first iteration's weight loads go out before the norm statistics.
-  if (wid < nchunks) load_w(wid);
+  const float* const xin = reinterpret_cast<const float*>(Ain);
+
+  // With the norm: this lane's residual values of the first iteration's two chunks are loaded
+  // first (the loop's element mapping, kept in registers for it), then the weights.  Loads
+  // complete in issue order, so the statistics below wait for x only, not for the weights.
+  float xa[NORM ? MR : 1][2][8];
+  if (NORM) {
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int k = min((wid + 4 * u) * KW + lane * 8, K - 8);
+        load8(xin + (size_t)(m0 + min(i, mrows - 1)) * K + k, xa[i][u]);
+      }
+  }
+  load_w(min(wid, nchunks - 1));
 
   float inv[MR];
   bool range_bad = false;
@@ -201,11 +215,22 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
 #pragma unroll
     for (int i = 0; i < MR; ++i) {
       ss[i] = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if ((wid + 4 * u) * KW + lane * 8 >= K) continue;  // clamped duplicate of another chunk
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss[i] = fmaf(xa[i][u][e], xa[i][u][e], ss[i]);
+      }
+      // rows longer than one iteration (K > 4096): the rest of this lane's chunks
       if (i < mrows) {
-        const float* xr = reinterpret_cast<const float*>(Ain) + (size_t)(m0 + i) * K;
-        for (int k = (wid * WAVE + lane) * 4; k < K; k += 256 * 4) {
-          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(xr + k);
-          ss[i] += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        for (int c = wid + 8; c < nchunks; c += 4) {
+          const int k = c * KW + lane * 8;
+          if (k < K) {
+            float a[8];
+            load8(xin + (size_t)(m0 + i) * K + k, a);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss[i] = fmaf(a[e], a[e], ss[i]);
+          }
         }
       }
       ss[i] = wave_sum(ss[i]);
@@ -223,7 +248,8 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   }
 
   for (int c0 = wid; c0 < nchunks; c0 += 8) {
-    if (c0 != wid) load_w(c0);
+    const bool first = c0 == wid;
+    if (!first) load_w(c0);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if (!ok[u]) continue;
@@ -236,7 +262,12 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
           uint32_t ah[4];
           if (NORM) {
             float a[8];
-            load8(reinterpret_cast<const float*>(Ain) + (size_t)(m0 + i) * K + kk[u], a);
+            if (first) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) a[e] = xa[i][u][e];
+            } else {
+              load8(xin + (size_t)(m0 + i) * K + kk[u], a);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               a[e] = a[e] * inv[i] * g[e];
