@@ -1,25 +1,30 @@
 #!/usr/bin/env python3
 """Throughput of the Llama decoder pass on one MI355X.
 
-Default workload (``--workload llama3-8b``): the Llama-3-8B shape (32 layers,
-dim 4096, 32 query / 8 KV heads, FFN 14336, vocab 128256, bf16 random-init
-weights ~ N(0, 0.02)), batch 1, a prompt of 512 token ids uniform in
-[0, 128256), prefill, then 256 greedy KV-cached decode steps replayed from the
-library's HIP graph.  One step = that whole job; the JSON line reports tokens/s
-over it plus prefill tok/s and decode tok/s separately.
+Headline workload (``llama3-8b``): the Llama-3-8B shape (32 layers, dim 4096,
+32 query / 8 KV heads, FFN 14336, vocab 128256, bf16 random-init weights
+~ N(0, 0.02)), batch 1, a prompt of 512 token ids uniform in [0, 128256),
+prefill, then 256 greedy KV-cached decode steps replayed from the library's HIP
+graph.  One step = that whole job; the JSON line reports tokens/s over it plus
+prefill tok/s and decode tok/s separately.
 
-Other workloads (opt-in, same JSON contract):
+The default run (``--workload all``) prints that headline line and adds, under
+``workloads``, one entry per other workload, each with its own steps, timing,
+``roofline`` and ``cpu_baseline``:
+  stories15m                fp32 stories15M shape: prefill of 8 ids + 50 greedy decode steps
+                            (latency / launch bound: us per step and kernels per step)
   llama3-8b-layer           one 8B-shaped layer on x ~ N(0,1) [2048, 4096] (prefill tok/s)
   llama3-8b-long-prefill    prefill of 8192 ids, last-position logits (prefill tok/s)
   llama3-8b-batched-decode  one decode step of 64 sequences, cached lengths U{1024..8192},
                             N(0,1) caches (decode tok/s)
+``--workload NAME`` runs one of them alone as the line's headline.
 
 Per-kernel durations come from the library's own hipEvent brackets (one extra,
 untimed pass with kernel timing on); ``roofline`` is for the workload's dominant
 kernel.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload and scales it to the full job.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -153,17 +158,33 @@ def time_steps(torch, step, steps: int, warmup: int):
 
 # ----------------------------------------------------------------------------- workloads
 
-def bench_generate(args, torch, B, inputs, LlamaModel) -> dict:
+def shared_8b_weights(args, inputs, shared):
+    """Device bf16 weights of the 32-layer Llama-3-8B shape and host copies of the first
+    layers, generated once and shared by the 8B workloads of one run."""
+    if "dw" not in shared:
+        shape = inputs.LLAMA3_8B if not args.layers else inputs.LLAMA3_8B.replace(n_layers=args.layers)
+        t0 = time.perf_counter()
+        keep = 0 if args.no_cpu_baseline else min(args.cpu_layers, shape.n_layers)
+        shared["dw"], shared["host"] = make_weights(shape, keep, keep_head=not args.no_cpu_baseline)
+        log(f"8B weights generated and uploaded in {time.perf_counter() - t0:.1f}s")
+    return shared["dw"], shared["host"]
+
+
+def release(torch):
+    """Return the memory of models the caller has just deleted."""
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def bench_generate(args, torch, B, inputs, LlamaModel, shared, steps: int, warmup: int) -> dict:
     wl = inputs.WORKLOADS["llama3-8b"]
     shape = wl.shape if not args.layers else wl.shape.replace(n_layers=args.layers)
     P, T = wl.prompt_len, wl.decode_steps
     dev = "cuda:0"
-    t0 = time.perf_counter()
-    dw, host_w = make_weights(shape, 0 if args.no_cpu_baseline else args.cpu_layers)
-    log(f"weights generated and uploaded in {time.perf_counter() - t0:.1f}s")
+    dw, host_w = shared_8b_weights(args, inputs, shared)
     model = LlamaModel(shape, dw, max_batch=1, max_prefill_tokens=P, device=dev)
-    del dw
-    torch.cuda.empty_cache()
 
     prompt_np = inputs.token_ids(shape.vocab_size, P)
     prompt = torch.as_tensor(prompt_np, device=dev)
@@ -188,18 +209,22 @@ def bench_generate(args, torch, B, inputs, LlamaModel) -> dict:
         ev[2].record(stream)
         evs.append(ev)
 
-    wall = time_steps(torch, step, args.steps, args.warmup)
-    evs = evs[args.warmup:]
+    wall = time_steps(torch, step, steps, warmup)
+    evs = evs[warmup:]
     prefill_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     assert model.read_device_error() == 0
-    log(f"timed {args.steps} steps in {wall:.3f}s: prefill {prefill_ms:.3f} ms, decode {decode_ms / T:.3f} ms/token")
+    log(f"llama3-8b: timed {steps} steps in {wall:.3f}s: prefill {prefill_ms:.3f} ms, decode {decode_ms / T:.3f} "
+        f"ms/token")
 
     kt_prefill = timed_groups(B, h, lambda: B.llm_prefill(h, 0, prompt, P, 0, logits1, stream))
     torch.cuda.synchronize()
     pos.fill_(P)
     kt_decode = timed_groups(B, h, lambda: B.llm_generate(h, 1, slots, pos, tok, T, out, logitsB, stream))
     torch.cuda.synchronize()
+    first_tokens = out[:8, 0].cpu().tolist()
+    del model
+    release(torch)
 
     L, dim, F, V = shape.n_layers, shape.dim, shape.ffn_hidden_dim, shape.vocab_size
     up_bytes = 2 * F * dim * 2 + 2 * dim * 4 + F * 2  # w1|w3 weights + fp32 x and norm weight in + SwiGLU row out
@@ -213,7 +238,7 @@ def bench_generate(args, torch, B, inputs, LlamaModel) -> dict:
     mean_ctx = P + (T - 1) / 2.0 + 1
     dec_bytes = w_bytes + kv_pos_bytes * mean_ctx
     res = {
-        "value": round((P + T) * args.steps / wall, 3), "unit": "tok/s", "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "value": round((P + T) * steps / wall, 3), "unit": "tok/s", "ms_per_step": round(wall / steps * 1e3, 3),
         "config": {"workload": "llama3-8b: 32-layer Llama-3-8B-shaped bf16 model, batch 1, prefill of 512 ids "
                                "then 256 greedy KV-cached decode steps",
                    "prompt_len": P, "decode_steps": T, "batch": 1, "parallelism": "none (1 GPU)"},
@@ -227,7 +252,7 @@ def bench_generate(args, torch, B, inputs, LlamaModel) -> dict:
         "roofline_prefill": mfma_roofline("prefill gate-up GEMM (M=512, N=28672, K=4096) + SwiGLU",
                                           2.0 * P * (2 * F) * dim, avg_ms(kt_prefill, "gate_up")),
         "per_kernel": per_kernel,
-        "generated_first_tokens": out[:8, 0].cpu().tolist(),
+        "generated_first_tokens": first_tokens,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_generate(shape, host_w, prompt_np, args.cpu_layers, args.cpu_decode_steps, T)
@@ -267,14 +292,104 @@ def cpu_generate(shape, host_w, prompt, n_layers_sample: int, decode_sample: int
             "sample_seconds": round(t2 - t0 + t_layers + t_head, 2)}
 
 
-def bench_layer(args, torch, B, inputs, LlamaModel) -> dict:
+def bench_stories(args, torch, B, inputs, LlamaModel, shared, steps: int, warmup: int) -> dict:
+    """stories15M fp32: prefill of 8 ids, then 50 greedy decode steps replayed from the graph.  The
+    97.6 MB model sits in the 256 MB memory-side cache, so the job is bound by latency and kernel
+    launches: the entry reports us per decode step and kernels per step; its HBM figure is context."""
+    wl = inputs.WORKLOADS["stories15m"]
+    shape = wl.shape
+    P, T = wl.prompt_len, wl.decode_steps
+    dev = "cuda:0"
+    hw = inputs.all_weights(shape)
+    model = LlamaModel(shape, {k: torch.from_numpy(v).to(dev) for k, v in hw.items()}, max_batch=1,
+                       max_prefill_tokens=P, device=dev)
+    prompt_np = inputs.token_ids(shape.vocab_size, P)
+    prompt = torch.as_tensor(prompt_np, device=dev)
+    slots = torch.zeros(1, dtype=torch.int32, device=dev)
+    pos = torch.zeros(1, dtype=torch.int32, device=dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    logits1 = torch.empty(shape.vocab_size, dtype=torch.float32, device=dev)
+    logitsB = torch.empty(1, shape.vocab_size, dtype=torch.float32, device=dev)
+    out = torch.empty(T, 1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    h = model.handle
+    evs = []
+
+    def step():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        B.llm_prefill(h, 0, prompt, P, 0, logits1, stream)
+        B.llm_argmax(logits1, 1, shape.vocab_size, tok, stream)
+        ev[1].record(stream)
+        pos.fill_(P)
+        B.llm_generate(h, 1, slots, pos, tok, T, out, logitsB, stream)
+        ev[2].record(stream)
+        evs.append(ev)
+
+    wall = time_steps(torch, step, steps, warmup)
+    evs = evs[warmup:]
+    prefill_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    assert model.read_device_error() == 0
+    # One more job with the kernel brackets on around the decode steps (direct launches).
+    B.llm_prefill(h, 0, prompt, P, 0, logits1, stream)
+    B.llm_argmax(logits1, 1, shape.vocab_size, tok, stream)
+    t0_gpu = int(tok.item())
+    pos.fill_(P)
+    B.llm_set_kernel_timing(h, True)
+    B.llm_generate(h, 1, slots, pos, tok, T, out, logitsB, stream)
+    groups = {name: B.llm_kernel_timing_full(h, k) for k, name in enumerate(B.KERNEL_GROUPS)}
+    B.llm_set_kernel_timing(h, False)
+    torch.cuda.synchronize()
+    gpu_tokens = [t0_gpu] + out[:, 0].cpu().tolist()
+    del model
+    release(torch)
+    kernels_per_step = sum(k for _, k, _ in groups.values()) / T
+    kernel_us_per_step = sum(ms for _, _, ms in groups.values()) * 1e3 / T
+    L, dim, F, V = shape.n_layers, shape.dim, shape.ffn_hidden_dim, shape.vocab_size
+    hd = shape.head_dim
+    w_bytes = 4 * (L * (dim * (shape.n_heads + 2 * shape.n_kv_heads) * hd + dim * shape.n_heads * hd + 3 * F * dim)
+                   + V * dim)
+    us_step = decode_ms / T * 1e3
+    res = {"value": round((P + T) * steps / wall, 1), "unit": "tok/s", "ms_per_step": round(wall / steps * 1e3, 3),
+           "steps": steps, "warmup": warmup, "dtype": "f32",
+           "config": {"workload": "stories15m: stories15M-shaped fp32 Llama (dim 288, 6 layers, 6 heads, vocab "
+                                  "32000), batch 1, prefill of 8 ids then 50 greedy KV-cached decode steps",
+                      "prompt_len": P, "decode_steps": T, "batch": 1},
+           "prefill_us": round(prefill_ms * 1e3, 1), "us_per_decode_step": round(us_step, 2),
+           "kernels_per_decode_step": round(kernels_per_step, 2),
+           "kernel_us_per_decode_step": round(kernel_us_per_step, 2),
+           "roofline": dict(hbm_roofline("whole decode step (latency / launch bound: the weights sit in the "
+                                         "memory-side cache; HBM figure is context only)", w_bytes, us_step * 1e-3),
+                            bound_note="latency"),
+           "generated_tokens": gpu_tokens[:8]}
+    if not args.no_cpu_baseline:
+        from oracle import OracleModel
+        om = OracleModel(oracle_cfg(shape, shape.n_layers), hw, dtype=np.float64)
+        times, toks = [], None
+        while len(times) < 20 and sum(times) < 5.0:
+            t0 = time.perf_counter()
+            toks, _ = om.generate(prompt_np, T)
+            times.append(time.perf_counter() - t0)
+        t = float(np.mean(times))
+        res["cpu_baseline"] = {"value": round((P + T) / t, 2), "unit": "tok/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": (f"the whole workload: oracle (numpy fp64) prefill of the 8 ids and 50 "
+                                          f"greedy decode steps, mean of {len(times)} passes"),
+                               "us_per_decode_step": round(t / (T + 1) * 1e6, 1),
+                               "sample_seconds": round(sum(times), 2)}
+        res["tokens_match_oracle"] = gpu_tokens == [int(v) for v in toks]
+    return res
+
+
+def bench_layer(args, torch, B, inputs, LlamaModel, shared, steps: int, warmup: int) -> dict:
     wl = inputs.WORKLOADS["llama3-8b-layer"]
     shape = wl.shape.replace(vocab_size=256)  # embedding / LM head unused by the layer
     S = wl.prompt_len
     dw, host_w = make_weights(shape, 1 if not args.no_cpu_baseline else 0, keep_head=False)
     model = LlamaModel(shape, dw, max_batch=1, max_prefill_tokens=S)
     del dw
-    torch.cuda.empty_cache()
+    release(torch)
     x0 = torch.from_numpy(inputs.bf16_bits_to_f32(inputs.activations_bf16_bits(S, shape.dim))).to("cuda:0")
     x = torch.empty_like(x0)
     stream = torch.cuda.current_stream()
@@ -289,13 +404,16 @@ def bench_layer(args, torch, B, inputs, LlamaModel) -> dict:
         ev[1].record(stream)
         evs.append(ev)
 
-    wall = time_steps(torch, step, args.steps, args.warmup)
-    layer_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs[args.warmup:]]))
+    wall = time_steps(torch, step, steps, warmup)
+    layer_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs[warmup:]]))
     x.copy_(x0)
     kt = timed_groups(B, h, lambda: B.llm_layer_forward(h, 0, 0, x, S, 0, stream))
+    del model
+    release(torch)
     lin, att = layer_flops(shape, S)
     F, dim = shape.ffn_hidden_dim, shape.dim
-    res = {"value": round(S * args.steps / wall, 1), "unit": "tok/s", "ms_per_step": round(wall / args.steps * 1e3, 3),
+    res = {"value": round(S * steps / wall, 1), "unit": "tok/s", "ms_per_step": round(wall / steps * 1e3, 3),
+           "steps": steps, "warmup": warmup,
            "config": {"workload": "llama3-8b-layer: one Llama-3-8B-shaped decoder layer, bf16 weights, "
                                   "x ~ N(0,1) bf16 [2048, 4096], positions 0..2047", "seq_len": S, "batch": 1,
                       "parallelism": "none (1 GPU)"},
@@ -329,27 +447,30 @@ def bench_layer(args, torch, B, inputs, LlamaModel) -> dict:
     return res
 
 
-def bench_long_prefill(args, torch, B, inputs, LlamaModel) -> dict:
+def bench_long_prefill(args, torch, B, inputs, LlamaModel, shared, steps: int, warmup: int) -> dict:
     wl = inputs.WORKLOADS["llama3-8b-long-prefill"]
-    shape = wl.shape
+    shape = wl.shape if not args.layers else wl.shape.replace(n_layers=args.layers)
     S = wl.prompt_len
     n_cpu = 0 if args.no_cpu_baseline else 2
-    dw, host_w = make_weights(shape, n_cpu, keep_head=not args.no_cpu_baseline)
+    dw, host_w = shared_8b_weights(args, inputs, shared)
     model = LlamaModel(shape, dw, max_batch=1, max_prefill_tokens=S)
-    del dw
-    torch.cuda.empty_cache()
     prompt_np = inputs.token_ids(shape.vocab_size, S)
     prompt = torch.as_tensor(prompt_np, device="cuda:0")
     logits = torch.empty(shape.vocab_size, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
     h = model.handle
-    wall = time_steps(torch, lambda: B.llm_prefill(h, 0, prompt, S, 0, logits, stream), args.steps, args.warmup)
+    wall = time_steps(torch, lambda: B.llm_prefill(h, 0, prompt, S, 0, logits, stream), steps, warmup)
+    assert model.read_device_error() == 0
     kt = timed_groups(B, h, lambda: B.llm_prefill(h, 0, prompt, S, 0, logits, stream))
+    del model
+    release(torch)
     lin, att = layer_flops(shape, S)
     total_flops = shape.n_layers * (lin + att) + 2.0 * shape.dim * shape.vocab_size
-    t_step = wall / args.steps
+    t_step = wall / steps
     F, dim = shape.ffn_hidden_dim, shape.dim
-    res = {"value": round(S * args.steps / wall, 1), "unit": "tok/s", "ms_per_step": round(t_step * 1e3, 3),
+    log(f"llama3-8b-long-prefill: {S * steps / wall:.0f} tok/s")
+    res = {"value": round(S * steps / wall, 1), "unit": "tok/s", "ms_per_step": round(t_step * 1e3, 3),
+           "steps": steps, "warmup": warmup,
            "config": {"workload": "llama3-8b-long-prefill: 32-layer Llama-3-8B-shaped bf16 model, prefill of 8192 "
                                   "ids, last-position logits", "seq_len": S, "batch": 1,
                       "parallelism": "none (1 GPU)"},
@@ -377,17 +498,15 @@ def bench_long_prefill(args, torch, B, inputs, LlamaModel) -> dict:
     return res
 
 
-def bench_batched_decode(args, torch, B, inputs, LlamaModel) -> dict:
+def bench_batched_decode(args, torch, B, inputs, LlamaModel, shared, steps: int, warmup: int) -> dict:
     from concurrent.futures import ThreadPoolExecutor
     wl = inputs.WORKLOADS["llama3-8b-batched-decode"]
-    shape = wl.shape
+    shape = wl.shape if not args.layers else wl.shape.replace(n_layers=args.layers)
     Bn = wl.batch
     lo, hi = wl.kv_len_range
-    n_cpu = 0 if args.no_cpu_baseline else 8
-    dw, host_w = make_weights(shape, n_cpu, keep_head=not args.no_cpu_baseline)
+    n_cpu = 0 if args.no_cpu_baseline else min(8, shape.n_layers)
+    dw, host_w = shared_8b_weights(args, inputs, shared)
     model = LlamaModel(shape, dw, max_batch=Bn, max_prefill_tokens=1)
-    del dw
-    torch.cuda.empty_cache()
     lengths = inputs.kv_lengths(Bn, lo, hi)
     kv = model.kv_cache_view()
     G, hd = shape.n_kv_heads, shape.head_dim
@@ -401,7 +520,7 @@ def bench_batched_decode(args, torch, B, inputs, LlamaModel) -> dict:
             for (w, b, g), blk in ex.map(gen, jobs):
                 kv[l, w, b, g, : lengths[b]] = torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16).to(
                     "cuda:0").to(kv.dtype)
-    log(f"cache contents generated in {time.perf_counter() - t0:.1f}s")
+    log(f"llama3-8b-batched-decode: cache contents generated in {time.perf_counter() - t0:.1f}s")
     toks = torch.as_tensor(inputs.token_ids(shape.vocab_size, Bn, sub=4), device="cuda:0")
     slots = torch.arange(Bn, dtype=torch.int32, device="cuda:0")
     pos = torch.as_tensor(lengths, device="cuda:0")
@@ -412,15 +531,19 @@ def bench_batched_decode(args, torch, B, inputs, LlamaModel) -> dict:
     def step():
         B.llm_decode_step(h, Bn, slots, pos, toks, logits, stream)
 
-    wall = time_steps(torch, step, args.steps, args.warmup)
+    wall = time_steps(torch, step, steps, warmup)
     assert model.read_device_error() == 0
     kt = timed_groups(B, h, step)
-    t_step = wall / args.steps
+    del kv, model
+    release(torch)
+    t_step = wall / steps
     L, dim, F, V = shape.n_layers, shape.dim, shape.ffn_hidden_dim, shape.vocab_size
     w_bytes = 2 * (L * (dim * (shape.n_heads + 2 * G) * hd + dim * shape.n_heads * hd + 3 * F * dim) + V * dim)
     kv_bytes = L * G * hd * 2 * 2 * float(np.sum(lengths.astype(np.int64) + 1))
     att_bytes_per_launch = kv_bytes / L
-    res = {"value": round(Bn * args.steps / wall, 1), "unit": "tok/s", "ms_per_step": round(t_step * 1e3, 3),
+    log(f"llama3-8b-batched-decode: {Bn * steps / wall:.0f} tok/s")
+    res = {"value": round(Bn * steps / wall, 1), "unit": "tok/s", "ms_per_step": round(t_step * 1e3, 3),
+           "steps": steps, "warmup": warmup,
            "config": {"workload": "llama3-8b-batched-decode: 32-layer Llama-3-8B-shaped bf16 model, one decode step "
                                   "for 64 sequences with cached lengths U{1024..8192}", "batch": Bn,
                       "parallelism": "none (1 GPU)"},
@@ -466,8 +589,11 @@ def bench_batched_decode(args, torch, B, inputs, LlamaModel) -> dict:
     return res
 
 
-WORKLOAD_FUNS = {"llama3-8b": bench_generate, "llama3-8b-layer": bench_layer,
+WORKLOAD_FUNS = {"llama3-8b": bench_generate, "stories15m": bench_stories, "llama3-8b-layer": bench_layer,
                  "llama3-8b-long-prefill": bench_long_prefill, "llama3-8b-batched-decode": bench_batched_decode}
+# Steps and warm-up of the workloads that ride along with the headline in the default run.
+EXTRA_STEPS = {"stories15m": (20, 3), "llama3-8b-layer": (20, 3), "llama3-8b-long-prefill": (5, 1),
+               "llama3-8b-batched-decode": (10, 2)}
 
 
 def main() -> int:
@@ -475,13 +601,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="llama3-8b", choices=sorted(WORKLOAD_FUNS))
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WORKLOAD_FUNS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=16, help="layers in the CPU oracle sample (llama3-8b)")
     ap.add_argument("--cpu-decode-steps", type=int, default=100, help="decode steps in the CPU oracle sample (llama3-8b)")
     ap.add_argument("--layers", type=int, default=0,
-                    help="profiling aid (llama3-8b workload only): build the model with this many layers; every "
-                         "kernel keeps its launch shape, but the line is then not the metric")
+                    help="profiling aid (8B workloads): build the models with this many layers; every kernel keeps "
+                         "its launch shape, but the line is then not the metric")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one plain elementwise pass over 1 GiB (torch.neg, fp32: reads 1 GiB, writes "
                          "1 GiB), the reference dispatch that scales the FETCH_SIZE / WRITE_SIZE counters of a "
@@ -498,7 +624,17 @@ def main() -> int:
     from llama_decoder_transformer_amd import inputs
     from llama_decoder_transformer_amd.model import LlamaModel
 
-    body = WORKLOAD_FUNS[args.workload](args, torch, B, inputs, LlamaModel)
+    shared = {}
+    head = "llama3-8b" if args.workload == "all" else args.workload
+    body = WORKLOAD_FUNS[head](args, torch, B, inputs, LlamaModel, shared, args.steps, args.warmup)
+    if args.workload == "all":
+        extra = {}
+        for name, (k, w) in EXTRA_STEPS.items():
+            t0 = time.perf_counter()
+            extra[name] = WORKLOAD_FUNS[name](args, torch, B, inputs, LlamaModel, shared, k, w)
+            log(f"{name} done in {time.perf_counter() - t0:.1f}s")
+        body["workloads"] = extra
+    shared.clear()
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
@@ -506,14 +642,18 @@ def main() -> int:
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    body.pop("steps", None)
+    body.pop("warmup", None)
+    dtype = body.pop("dtype", "f16")
     res = {"metric": METRIC, "value": body.pop("value"), "unit": body.pop("unit"), "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": body.pop("ms_per_step"), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-           "dtype_note": "fp16 MFMA operands with fp32 accumulation; bf16 weights held exactly as fp16; fp32 residual",
+           "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+           "dtype_note": ("fp32 throughout" if dtype == "f32" else
+                          "fp16 MFMA operands with fp32 accumulation; bf16 weights held as fp16; fp32 residual"),
            "data": "synthetic", "config": body.pop("config")}
     res.update(body)
     if args.layers:
-        res["profiling_only"] = f"model built with {args.layers} layers instead of the workload's; not the metric"
+        res["profiling_only"] = f"models built with {args.layers} layers instead of the workload's; not the metric"
     print(json.dumps(res), flush=True)
     return 0
 
