@@ -229,6 +229,24 @@ llm_status llm_decode_step(llm_model* m, int32_t batch, const int32_t* slots_dev
                            float* logits_dev, void* stream);
 
 /*
+ * llm_decode_step for callers that cannot allocate device memory at all (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step and the same results, with the kernels' scratch (the split-KV attention chunk
+ * partials and the split-K projection partials) in a static device array of the library
+ * instead of regions of the model's workspace.  That array holds 32 MiB on each GPU the
+ * library runs on, until the process ends; a step whose partials need more (the
+ * message states how much) is rejected with LLM_ERR_OUT_OF_RANGE before anything is
+ * enqueued.  (A Llama-3-8B-shaped step of 64 rows over an 8193-position cache needs
+ * about 14 MB.)  The call enqueues kernels only: no allocation, no synchronisation.
+ * Every call on one GPU shares that GPU's array, and no value in it needs to start at
+ * zero (each partial is written before it is read); calls that overlap on one GPU, from
+ * several streams or threads, race on it.  Arguments and errors as llm_decode_step.
+ */
+llm_status llm_decode_step_noalloc(llm_model* m, int32_t batch, const int32_t* slots_dev,
+                                   const int32_t* positions_dev, const int32_t* tokens_dev,
+                                   float* logits_dev, void* stream);
+
+/*
  * Greedy choice ("Predicción de tokens": the token with the highest logit):
  * out_dev[r] = argmax over logits_dev[r*vocab .. r*vocab+vocab-1], lowest index
  * on ties.  logits_dev device fp32 [rows, vocab]; out_dev device int32 [rows].

@@ -27,7 +27,7 @@ DEVERR_TOKEN, DEVERR_POSITION, DEVERR_SLOT, DEVERR_RANGE = 1, 2, 4, 8
 
 EXPORTED = ("llm_check_config", "llm_packed_weight_bytes", "llm_kv_cache_bytes", "llm_workspace_bytes",
             "llm_init_weights", "llm_prefill", "llm_prefill_batch", "llm_layer_forward", "llm_decode_step",
-            "llm_argmax",
+            "llm_decode_step_noalloc", "llm_argmax",
             "llm_generate", "llm_read_device_error", "llm_set_kernel_timing", "llm_kernel_timing",
             "llm_free", "llm_status_string", "llm_last_error_message")
 KERNEL_GROUPS = ("embed", "rmsnorm", "qkv", "attn", "wo", "gate_up", "down", "lm_head", "argmax")
@@ -82,6 +82,8 @@ def lib():
                                             c_void_p, c_void_p, c_void_p]),
             "llm_layer_forward": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p]),
             "llm_decode_step": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+            "llm_decode_step_noalloc": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                  c_void_p]),
             "llm_argmax": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
             "llm_generate": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                        c_void_p, c_void_p]),
@@ -167,6 +169,11 @@ def llm_layer_forward(handle: int, layer: int, slot: int, x, n_tokens: int, star
 def llm_decode_step(handle: int, batch: int, slots, positions, tokens, logits, stream=None) -> None:
     _check(lib().llm_decode_step(handle, batch, _ptr(slots), _ptr(positions), _ptr(tokens), _ptr(logits),
                                  _stream(stream)))
+
+
+def llm_decode_step_noalloc(handle: int, batch: int, slots, positions, tokens, logits, stream=None) -> None:
+    _check(lib().llm_decode_step_noalloc(handle, batch, _ptr(slots), _ptr(positions), _ptr(tokens), _ptr(logits),
+                                         _stream(stream)))
 
 
 def llm_argmax(logits, rows: int, vocab: int, out, stream=None) -> None:

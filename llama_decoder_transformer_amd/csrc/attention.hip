@@ -874,6 +874,19 @@ static bool attn_decode_mfma(const f16_t* q, const f16_t* kc, const f16_t* vc, c
   return true;
 }
 
+size_t attn_decode_partial_floats_used(int dtype, int rows, int n_heads, int n_kv_heads, int head_dim, int max_seq) {
+  if (rows <= 0) return 0;
+  int nch = 1;
+  if (dtype == 1 && head_dim == PF_D && n_heads / n_kv_heads <= DM_MAXH) {
+    const int ch = dec_mfma_chunk(rows, n_kv_heads, max_seq);
+    nch = (max_seq + ch - 1) / ch;
+  } else if (!dec_single_pass(rows, n_heads, max_seq)) {
+    const int ch = attn_decode_chunk(rows, n_kv_heads, max_seq);
+    nch = (max_seq + ch - 1) / ch;
+  }
+  return nch > 1 ? (size_t)rows * n_heads * nch * (head_dim + 2) : 0;
+}
+
 bool attn_prefill_supported(int head_dim, int n_heads, int n_kv_heads) {
   if (head_dim != PF_D || n_kv_heads <= 0 || n_heads % n_kv_heads) return false;
   const int hpg = n_heads / n_kv_heads;

@@ -103,6 +103,8 @@ void launch_gemv(int dtype, const void* A, const void* W, const float* norm_w, f
 // attn_decode_partial_floats(...) floats.
 int attn_decode_chunk(int rows, int n_kv_heads, int max_seq);
 size_t attn_decode_partial_floats(int rows, int n_heads, int head_dim, int max_seq);
+// The partial floats the launcher actually uses for `rows` decode rows (its own chunk choice).
+size_t attn_decode_partial_floats_used(int dtype, int rows, int n_heads, int n_kv_heads, int head_dim, int max_seq);
 void launch_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
                         const int* row_pos, const int* row_slot, int pos0, int slot0, int rows,
                         int n_heads, int n_kv_heads, int head_dim, int max_seq, int n_slots,

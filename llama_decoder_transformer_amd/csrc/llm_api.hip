@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -11,6 +12,14 @@
 #include "llm.h"
 
 using namespace llm;
+
+// Scratch of llm_decode_step_noalloc: the split-KV attention and split-K projection partials
+// of one decode step, in a file-scope device array instead of the caller's workspace, so the
+// call needs no allocation by anyone.  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never uses this name as an address: it resolves the array's
+// address on each device once (noalloc_scratch_ptr) and passes that to the kernels.
+constexpr size_t LLM_NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[LLM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -273,18 +282,29 @@ EpiParams base_epi(llm_model* m) {
 
 bool use_mfma(const llm_model* m, int M) { return m->cfg.dtype == LLM_BF16 && M > 8; }
 
+// Scratch of the kernels that merge partial results: the split-KV attention chunks and the
+// split-K projection slices.  Normally regions of the caller's workspace; the static device
+// array for llm_decode_step_noalloc.
+struct Partials {
+  float* attn;
+  float* splitk;
+  size_t splitk_floats;
+};
+
+Partials ws_partials(const llm_model* m) { return Partials{m->attn, m->splitk, m->splitk_floats}; }
+
 // y = A W^T with epilogue `ep`.  With norm_w, A is the fp32 residual stream and the
 // projection consumes rmsnorm(A) * norm_w: fused into the GEMV, or a separate RMSNorm
 // into m->a ahead of the MFMA GEMM.
 void project(llm_model* m, const void* A, const void* W, int M, int N, int K, const EpiParams& ep, hipStream_t s,
-             const float* norm_w = nullptr) {
+             const Partials& pt, const float* norm_w = nullptr) {
   const llm_config& c = m->cfg;
   if (use_mfma(m, M)) {
     if (norm_w) {
       launch_rmsnorm(c.dtype, (const float*)A, norm_w, M, K, c.norm_eps, m->a, m->flags, s);
       A = m->a;
     }
-    launch_gemm_f16(A, W, M, N, K, ep, m->splitk, m->splitk_floats, s);
+    launch_gemm_f16(A, W, M, N, K, ep, pt.splitk, pt.splitk_floats, s);
   } else {
     launch_gemv(c.dtype, A, W, norm_w, c.norm_eps, M, N, K, ep, s);
   }
@@ -305,7 +325,7 @@ struct Varlen {
 // Returns whether m->a now holds rmsnorm(x) with next_norm.  The two RMSNorms ahead of MFMA
 // projections ride in the split-K reduction of the wo / down projection when that is split.
 bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_slot, int pos0, int slot0,
-               bool prefill, hipStream_t s, const Varlen* vl = nullptr, bool a_ready = false,
+               bool prefill, hipStream_t s, const Partials& pt, const Varlen* vl = nullptr, bool a_ready = false,
                const float* next_norm = nullptr) {
   const llm_config& c = m->cfg;
   const LayerPtrs& L = m->layers[l];
@@ -324,9 +344,9 @@ bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   {
     Timed t(m, LLM_K_QKV, s);
     if (a_ready)
-      launch_gemm_f16(m->a, L.wqkv, M, (H + 2 * G) * hd, dim, e, m->splitk, m->splitk_floats, s);
+      launch_gemm_f16(m->a, L.wqkv, M, (H + 2 * G) * hd, dim, e, pt.splitk, pt.splitk_floats, s);
     else
-      project(m, m->x, L.wqkv, M, (H + 2 * G) * hd, dim, e, s, L.attn_norm);
+      project(m, m->x, L.wqkv, M, (H + 2 * G) * hd, dim, e, s, pt, L.attn_norm);
   }
 
   {
@@ -338,7 +358,7 @@ bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
       launch_attn_prefill(m->q, k_section(m, l), v_section(m, l), slot0, pos0, M, H, G, hd, c.max_seq_len, m->o, s);
     else
       launch_attn_decode(c.dtype, m->q, k_section(m, l), v_section(m, l), row_pos, row_slot, pos0, slot0, M, H, G,
-                         hd, c.max_seq_len, c.max_batch, m->attn, m->o, m->flags, s);
+                         hd, c.max_seq_len, c.max_batch, pt.attn, m->o, m->flags, s);
   }
 
   EpiParams r = base_epi(m);
@@ -349,9 +369,9 @@ bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   {
     Timed t(m, LLM_K_WO, s);
     if (use_mfma(m, M))
-      ffn_ready = launch_gemm_f16_resid_norm(m->o, L.wo, M, dim, H * hd, r, L.ffn_norm, c.norm_eps, m->a, m->splitk,
-                                             m->splitk_floats, s);
-    if (!ffn_ready) project(m, m->o, L.wo, M, dim, H * hd, r, s);
+      ffn_ready = launch_gemm_f16_resid_norm(m->o, L.wo, M, dim, H * hd, r, L.ffn_norm, c.norm_eps, m->a, pt.splitk,
+                                             pt.splitk_floats, s);
+    if (!ffn_ready) project(m, m->o, L.wo, M, dim, H * hd, r, s, pt);
   }
 
   EpiParams g = base_epi(m);
@@ -361,18 +381,18 @@ bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   {
     Timed t(m, LLM_K_GATE_UP, s);
     if (ffn_ready)
-      launch_gemm_f16(m->a, L.w13, M, 2 * F, dim, g, m->splitk, m->splitk_floats, s);
+      launch_gemm_f16(m->a, L.w13, M, 2 * F, dim, g, pt.splitk, pt.splitk_floats, s);
     else
-      project(m, m->x, L.w13, M, 2 * F, dim, g, s, L.ffn_norm);
+      project(m, m->x, L.w13, M, 2 * F, dim, g, s, pt, L.ffn_norm);
   }
 
   bool next_ready = false;
   {
     Timed t(m, LLM_K_DOWN, s);
     if (next_norm && use_mfma(m, M))
-      next_ready = launch_gemm_f16_resid_norm(m->u, L.w2, M, dim, F, r, next_norm, c.norm_eps, m->a, m->splitk,
-                                              m->splitk_floats, s);
-    if (!next_ready) project(m, m->u, L.w2, M, dim, F, r, s);
+      next_ready = launch_gemm_f16_resid_norm(m->u, L.w2, M, dim, F, r, next_norm, c.norm_eps, m->a, pt.splitk,
+                                              pt.splitk_floats, s);
+    if (!next_ready) project(m, m->u, L.w2, M, dim, F, r, s, pt);
   }
   return next_ready;
 }
@@ -380,12 +400,48 @@ bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
 // All layers over M rows, each passing its successor the attention-normed activations when its
 // down projection produced them.
 void run_layers(llm_model* m, int M, const int* row_pos, const int* row_slot, int pos0, int slot0, bool prefill,
-                hipStream_t s, const Varlen* vl = nullptr) {
+                hipStream_t s, const Partials& pt, const Varlen* vl = nullptr) {
   const int n = m->cfg.n_layers;
   bool a_ready = false;
   for (int l = 0; l < n; ++l)
-    a_ready = run_layer(m, l, M, row_pos, row_slot, pos0, slot0, prefill, s, vl, a_ready,
+    a_ready = run_layer(m, l, M, row_pos, row_slot, pos0, slot0, prefill, s, pt, vl, a_ready,
                         l + 1 < n ? m->layers[l + 1].attn_norm : nullptr);
+}
+
+// Device address of `scratch` on the current device, resolved once per device with that device
+// current (each GPU holds its own copy at its own address).
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // by device ordinal
+
+hipError_t noalloc_scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Partial floats a decode step of `batch` rows needs: the attention chunks its launcher picks,
+// and the largest split-K slice set of its projections (the bound launch_gemm_f16 plans with).
+void decode_partials_need(const llm_model* m, int batch, size_t* attn_floats, size_t* splitk_floats) {
+  const llm_config& c = m->cfg;
+  const int hd = m->hd, H = c.n_heads, G = c.n_kv_heads;
+  *attn_floats = attn_decode_partial_floats_used(c.dtype, batch, H, G, hd, c.max_seq_len);
+  size_t sk = 0;
+  if (use_mfma(m, batch)) {
+    const int shapes[5][2] = {{(H + 2 * G) * hd, c.dim}, {c.dim, H * hd}, {2 * c.ffn_hidden_dim, c.dim},
+                              {c.dim, c.ffn_hidden_dim}, {c.vocab_size, c.dim}};
+    for (auto& sh : shapes) sk = std::max(sk, gemm_splitk_floats(batch, sh[0], sh[1]));
+  }
+  *splitk_floats = sk;
 }
 
 llm_status hip_check(const char* what) {
@@ -395,25 +451,25 @@ llm_status hip_check(const char* what) {
 }
 
 // Final RMSNorm of `rows` rows starting at x_row0, then the output projection.
-void lm_head(llm_model* m, const float* x_rows, int rows, float* logits, hipStream_t s) {
+void lm_head(llm_model* m, const float* x_rows, int rows, float* logits, hipStream_t s, const Partials& pt) {
   const llm_config& c = m->cfg;
   Timed t(m, LLM_K_LM_HEAD, s);
   EpiParams e = base_epi(m);
   e.kind = EPI_STORE_F32;
   e.out_f32 = logits;
   e.ld = c.vocab_size;
-  project(m, x_rows, m->out_w, rows, c.vocab_size, c.dim, e, s, m->final_norm);
+  project(m, x_rows, m->out_w, rows, c.vocab_size, c.dim, e, s, pt, m->final_norm);
 }
 
 void enqueue_decode(llm_model* m, int batch, const int* slots, const int* positions, const int* tokens, float* logits,
-                    hipStream_t s) {
+                    hipStream_t s, const Partials& pt) {
   const llm_config& c = m->cfg;
   {
     Timed t(m, LLM_K_EMBED, s);
     launch_embed(c.dtype, m->emb, tokens, batch, c.dim, c.vocab_size, m->x, m->flags, s);
   }
-  run_layers(m, batch, positions, slots, 0, 0, false, s);
-  lm_head(m, m->x, batch, logits, s);
+  run_layers(m, batch, positions, slots, 0, 0, false, s, pt);
+  lm_head(m, m->x, batch, logits, s, pt);
 }
 
 }  // namespace
@@ -556,6 +612,10 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   if (e == hipSuccess) e = hipGetLastError();
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
+  // Resolve llm_decode_step_noalloc's static array on this device now; a failure here is
+  // reported by that call (which retries), not by the model's creation.
+  void* scratch_dev = nullptr;
+  if (e == hipSuccess && noalloc_scratch_ptr(&scratch_dev) != hipSuccess) (void)hipGetLastError();
   if (e != hipSuccess) {
     delete m;
     return fail(LLM_ERR_HIP, std::string("init: ") + hipGetErrorString(e));
@@ -578,8 +638,8 @@ llm_status llm_prefill(llm_model* m, int32_t slot, const int32_t* tokens_dev, in
     Timed t(m, LLM_K_EMBED, s);
     launch_embed(c.dtype, m->emb, tokens_dev, n_tokens, c.dim, c.vocab_size, m->x, m->flags, s);
   }
-  run_layers(m, n_tokens, nullptr, nullptr, start_pos, slot, true, s);
-  lm_head(m, m->x + (size_t)(n_tokens - 1) * c.dim, 1, logits_dev, s);
+  run_layers(m, n_tokens, nullptr, nullptr, start_pos, slot, true, s, ws_partials(m));
+  lm_head(m, m->x + (size_t)(n_tokens - 1) * c.dim, 1, logits_dev, s, ws_partials(m));
   return hip_check("prefill launch");
 }
 
@@ -641,9 +701,9 @@ llm_status llm_prefill_batch(llm_model* m, int32_t batch, const int32_t* slots_h
     launch_embed(c.dtype, m->emb, tokens_dev, T, c.dim, c.vocab_size, m->x, m->flags, s);
   }
   const Varlen vl{m->seqtab, batch, n_blocks, max_n};
-  run_layers(m, T, row_pos, row_slot, 0, 0, true, s, &vl);
+  run_layers(m, T, row_pos, row_slot, 0, 0, true, s, ws_partials(m), &vl);
   launch_gather_rows(m->x, last_idx, batch, c.dim, m->last, s);
-  lm_head(m, m->last, batch, logits_dev, s);
+  lm_head(m, m->last, batch, logits_dev, s, ws_partials(m));
   return hip_check("batched prefill launch");
 }
 
@@ -660,7 +720,7 @@ llm_status llm_layer_forward(llm_model* m, int32_t layer, int32_t slot, float* x
   hipStream_t s = as_stream(stream);
   hipError_t e = hipMemcpyAsync(m->x, x_dev, (size_t)n_tokens * c.dim * 4, hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess) return fail(LLM_ERR_HIP, hipGetErrorString(e));
-  run_layer(m, layer, n_tokens, nullptr, nullptr, start_pos, slot, true, s);
+  run_layer(m, layer, n_tokens, nullptr, nullptr, start_pos, slot, true, s, ws_partials(m));
   e = hipMemcpyAsync(x_dev, m->x, (size_t)n_tokens * c.dim * 4, hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess) return fail(LLM_ERR_HIP, hipGetErrorString(e));
   return hip_check("layer launch");
@@ -672,7 +732,31 @@ llm_status llm_decode_step(llm_model* m, int32_t batch, const int32_t* slots_dev
     return fail(LLM_ERR_INVALID_ARG, "NULL model or buffer");
   if (batch < 1) return fail(LLM_ERR_INVALID_ARG, "batch must be >= 1");
   if (batch > m->cfg.max_batch) return fail(LLM_ERR_OUT_OF_RANGE, "batch > max_batch");
-  enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, as_stream(stream));
+  enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, as_stream(stream), ws_partials(m));
+  return hip_check("decode launch");
+}
+
+llm_status llm_decode_step_noalloc(llm_model* m, int32_t batch, const int32_t* slots_dev,
+                                   const int32_t* positions_dev, const int32_t* tokens_dev, float* logits_dev,
+                                   void* stream) {
+  if (!m || !slots_dev || !positions_dev || !tokens_dev || !logits_dev)
+    return fail(LLM_ERR_INVALID_ARG, "NULL model or buffer");
+  if (batch < 1) return fail(LLM_ERR_INVALID_ARG, "batch must be >= 1");
+  if (batch > m->cfg.max_batch) return fail(LLM_ERR_OUT_OF_RANGE, "batch > max_batch");
+  size_t attn_f = 0, splitk_f = 0;
+  decode_partials_need(m, batch, &attn_f, &splitk_f);
+  const size_t attn_bytes = align256(attn_f * sizeof(float));
+  const size_t need = attn_bytes + splitk_f * sizeof(float);
+  if (need > LLM_NOALLOC_SCRATCH_BYTES)
+    return fail(LLM_ERR_OUT_OF_RANGE, "a decode step of " + std::to_string(batch) + " rows needs " +
+                                          std::to_string(need) + " bytes of scratch, more than the " +
+                                          std::to_string(LLM_NOALLOC_SCRATCH_BYTES) +
+                                          " the library holds for llm_decode_step_noalloc");
+  void* base = nullptr;
+  const hipError_t e = noalloc_scratch_ptr(&base);
+  if (e != hipSuccess) return fail(LLM_ERR_HIP, std::string("static scratch address: ") + hipGetErrorString(e));
+  const Partials pt{(float*)base, (float*)((char*)base + attn_bytes), splitk_f};
+  enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, as_stream(stream), pt);
   return hip_check("decode launch");
 }
 
@@ -704,7 +788,7 @@ llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev, i
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed);
     if (e == hipSuccess) {
-      enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, m->cap_stream);
+      enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, m->cap_stream, ws_partials(m));
       launch_argmax(logits_dev, batch, m->cfg.vocab_size, m->amax, tokens_dev, m->cap_stream);
       launch_advance(positions_dev, tokens_dev, out_tokens_dev, step, batch, m->cap_stream);
       e = hipStreamEndCapture(m->cap_stream, &graph);
@@ -731,7 +815,7 @@ llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev, i
       hipError_t e = hipGraphLaunch(exec, s);
       if (e != hipSuccess) return fail(LLM_ERR_HIP, std::string("graph launch: ") + hipGetErrorString(e));
     } else {
-      enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, s);
+      enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, s, ws_partials(m));
       Timed t(m, LLM_K_ARGMAX, s);
       launch_argmax(logits_dev, batch, m->cfg.vocab_size, m->amax, tokens_dev, s);
       launch_advance(positions_dev, tokens_dev, out_tokens_dev, step, batch, s);
