@@ -77,8 +77,11 @@ enum { LLM_F32 = 0, LLM_BF16 = 1 };
  * TOKEN a token id outside [0, vocab_size); POSITION a decode position outside
  * [0, max_seq_len); SLOT a decode slot outside [0, max_batch); RANGE a value
  * stored as fp16 (a packed weight, a normalised activation, q/k/v, a KV-cache
- * entry or a SwiGLU output) fell outside fp16's finite range or was NaN. */
-enum { LLM_DEVERR_TOKEN = 1, LLM_DEVERR_POSITION = 2, LLM_DEVERR_SLOT = 4, LLM_DEVERR_RANGE = 8 };
+ * entry or a SwiGLU output) fell outside fp16's finite range or was NaN; SYNC a
+ * kernel whose workgroups wait for one another gave up waiting (its wait is bounded,
+ * so the kernel always ends; the results of that step are not valid). */
+enum { LLM_DEVERR_TOKEN = 1, LLM_DEVERR_POSITION = 2, LLM_DEVERR_SLOT = 4, LLM_DEVERR_RANGE = 8,
+       LLM_DEVERR_SYNC = 16 };
 
 /*
  * Model hyper-parameters: the params.json field set printed on the "Building
@@ -285,7 +288,9 @@ llm_status llm_read_device_error(llm_model* m, int32_t* flags, void* stream);
  */
 enum {
   LLM_K_EMBED = 0, LLM_K_RMSNORM = 1, LLM_K_QKV = 2, LLM_K_ATTN = 3, LLM_K_WO = 4,
-  LLM_K_GATE_UP = 5, LLM_K_DOWN = 6, LLM_K_LM_HEAD = 7, LLM_K_ARGMAX = 8, LLM_K_COUNT = 9
+  LLM_K_GATE_UP = 5, LLM_K_DOWN = 6, LLM_K_LM_HEAD = 7, LLM_K_ARGMAX = 8,
+  LLM_K_DECODE_BLOCK = 9, /* batch-1 decode: q|k|v, attention and wo in one launch */
+  LLM_K_COUNT = 10
 };
 llm_status llm_set_kernel_timing(llm_model* m, int32_t enable);
 llm_status llm_kernel_timing(llm_model* m, int32_t kind, int64_t* launches, int64_t* kernels, double* total_ms);

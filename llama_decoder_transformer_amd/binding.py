@@ -23,14 +23,14 @@ LLM_F32 = 0
 LLM_BF16 = 1
 STATUS = {0: "LLM_OK", -1: "LLM_ERR_INVALID_ARG", -2: "LLM_ERR_CONFIG", -3: "LLM_ERR_OUT_OF_RANGE",
           -4: "LLM_ERR_BUFFER_TOO_SMALL", -5: "LLM_ERR_HIP"}
-DEVERR_TOKEN, DEVERR_POSITION, DEVERR_SLOT, DEVERR_RANGE = 1, 2, 4, 8
+DEVERR_TOKEN, DEVERR_POSITION, DEVERR_SLOT, DEVERR_RANGE, DEVERR_SYNC = 1, 2, 4, 8, 16
 
 EXPORTED = ("llm_check_config", "llm_packed_weight_bytes", "llm_kv_cache_bytes", "llm_workspace_bytes",
             "llm_init_weights", "llm_prefill", "llm_prefill_batch", "llm_layer_forward", "llm_decode_step",
             "llm_decode_step_noalloc", "llm_argmax",
             "llm_generate", "llm_read_device_error", "llm_set_kernel_timing", "llm_kernel_timing",
             "llm_free", "llm_status_string", "llm_last_error_message")
-KERNEL_GROUPS = ("embed", "rmsnorm", "qkv", "attn", "wo", "gate_up", "down", "lm_head", "argmax")
+KERNEL_GROUPS = ("embed", "rmsnorm", "qkv", "attn", "wo", "gate_up", "down", "lm_head", "argmax", "decode_block")
 
 
 class LibraryMissing(RuntimeError):

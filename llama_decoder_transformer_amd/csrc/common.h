@@ -19,6 +19,8 @@ constexpr int WAVE = 64;
 // Device error bit (LLM_DEVERR_RANGE in llm.h): a value stored as fp16 was outside fp16's
 // finite range (it became +-inf) or was not a number.
 constexpr int LLM_DEVERR_RANGE_BIT = 8;
+// Device error bit (LLM_DEVERR_SYNC in llm.h): a bounded wait inside a kernel gave up.
+constexpr int LLM_DEVERR_SYNC_BIT = 16;
 
 // True when fp16(v) is not finite: |v| rounds past the largest fp16 value (65504) or v is NaN.
 __device__ __forceinline__ bool f16_out_of_range(float v) { return !(__builtin_fabsf(v) < 65520.0f); }

@@ -11,8 +11,11 @@ namespace llm {
 // (embedding lookup of the "Building llama3 from scratch" page).
 template <typename TW>
 __global__ void __launch_bounds__(256) embed_kernel(const TW* __restrict__ emb, const int* __restrict__ tok,
-                                                    int dim, int vocab, float* __restrict__ x, int* err) {
+                                                    int dim, int vocab, float* __restrict__ x, int* err, int* zero,
+                                                    int n_zero, int zero_stride) {
   const int m = blockIdx.x;
+  if (m == 0)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[(size_t)i * zero_stride] = 0;
   const int t = tok[m];
   float* xr = x + (size_t)m * dim;
   if (t < 0 || t >= vocab) {
@@ -28,12 +31,15 @@ __global__ void __launch_bounds__(256) embed_kernel(const TW* __restrict__ emb, 
 }
 
 void launch_embed(int dtype, const void* emb, const int* tokens, int M, int dim, int vocab, float* x,
-                  int* err, hipStream_t s) {
+                  int* err, hipStream_t s, int* zero, int n_zero, int zero_stride) {
   if (M <= 0) return;
+  if (!zero) n_zero = 0;
   if (dtype == 1)
-    launch_k(embed_kernel<f16_t>, M, 256, 0, s, (const f16_t*)emb, tokens, dim, vocab, x, err);
+    launch_k(embed_kernel<f16_t>, M, 256, 0, s, (const f16_t*)emb, tokens, dim, vocab, x, err, zero, n_zero,
+             zero_stride);
   else
-    launch_k(embed_kernel<float>, M, 256, 0, s, (const float*)emb, tokens, dim, vocab, x, err);
+    launch_k(embed_kernel<float>, M, 256, 0, s, (const float*)emb, tokens, dim, vocab, x, err, zero, n_zero,
+             zero_stride);
 }
 
 // ---------------------------------------------------------------- RMSNorm

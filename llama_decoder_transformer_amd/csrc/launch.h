@@ -53,9 +53,10 @@ struct EpiParams {
   int* err;
 };
 
-// Embedding gather: x[m][:] = float(E[tok[m]][:]).
+// Embedding gather: x[m][:] = float(E[tok[m]][:]).  It also clears n_zero ints at zero[i * zero_stride]
+// (the decode block's counters of every layer) for the step it starts.
 void launch_embed(int dtype, const void* emb, const int* tokens, int M, int dim, int vocab, float* x,
-                  int* err, hipStream_t s);
+                  int* err, hipStream_t s, int* zero = nullptr, int n_zero = 0, int zero_stride = 1);
 // RMSNorm of fp32 rows into the activation dtype (an fp16 result out of range sets err bit 8).
 void launch_rmsnorm(int dtype, const float* x, const float* w, int M, int dim, float eps, void* out, int* err,
                     hipStream_t s);
@@ -129,6 +130,35 @@ int attn_prefill_block_rows(int max_n, int n_heads, int n_kv_heads);
 void launch_attn_prefill_varlen(const void* q, const void* k_cache, const void* v_cache, const SeqDesc* seqs,
                                 int nseq, int n_blocks, int max_n, int n_heads, int n_kv_heads, int head_dim,
                                 int max_seq, void* out, hipStream_t s);
+// Ints between two cross-workgroup counters of the decode block (one 128-byte line each).
+constexpr int DB_SYNC_LINE = 32;
+// Batch-1 decode of one layer's attention half in one launch: q|k|v GEMV (RMSNorm fused, RoPE,
+// cache write), causal GQA attention over the cache, wo GEMV with the residual add.
+struct DecodeBlockParams {
+  float* x;                // fp32 residual [dim]: the norm's input, then += o W_o^T
+  const float* attn_norm;  // fp32 [dim]
+  const _Float16* wqkv;    // [(H + 2G) * 128][dim]
+  const _Float16* wo;      // [dim][H * 128]
+  _Float16* q;             // [H * 128]
+  _Float16* o;             // [H * 128]
+  _Float16* kc;            // this layer's K section [slots][G][max_seq][128]
+  _Float16* vc;
+  const float* rope_cos;   // [max_seq][64]
+  const float* rope_sin;
+  const int* row_pos;      // device [1]
+  const int* row_slot;     // device [1]
+  float* partial;          // >= decode_block_partial_floats(H, max_seq) floats
+  int* sync;               // this layer's decode_block_sync_ints(G) ints, zero at the launch
+  int* err;
+  float eps;
+  int dim, H, G, max_seq, n_slots;
+  int nq, na, nch, qkv_per_group;  // set by the launcher
+};
+bool decode_block_supported(int dtype, int dim, int n_heads, int n_kv_heads);
+int decode_block_sync_ints(int n_kv_heads);
+size_t decode_block_partial_floats(int n_heads, int max_seq);
+void launch_decode_block(DecodeBlockParams p, hipStream_t s);
+
 // Per-row positions and slots, last-row indices and the device copy of up to SEQ_META_CHUNK
 // sequence descriptors, taken from the kernel arguments (no host staging buffer): entries
 // first .. first + count - 1 of the batch.

@@ -94,7 +94,7 @@ struct PackedLayout {
 
 // Workspace layout.
 struct WorkLayout {
-  size_t flags, x, a, q, o, u, attn, amax, splitk, splitk_floats, rowmeta, seqtab, last, total;
+  size_t flags, x, a, q, o, u, attn, amax, splitk, splitk_floats, rowmeta, seqtab, last, sync, total;
   explicit WorkLayout(const llm_config& c) {
     Dims d(c);
     const size_t R = (size_t)d.rows();
@@ -107,7 +107,8 @@ struct WorkLayout {
     q = p; p = align256(p + R * d.H * d.hd * d.es);
     o = p; p = align256(p + R * d.H * d.hd * d.es);
     u = p; p = align256(p + R * d.F * d.es);
-    attn = p; p = align256(p + attn_decode_partial_floats(att_rows, d.H, d.hd, d.S) * 4);
+    attn = p; p = align256(p + std::max(attn_decode_partial_floats(att_rows, d.H, d.hd, d.S),
+                                        decode_block_partial_floats(d.H, d.S)) * 4);
     amax = p; p = align256(p + (size_t)d.B * argmax_blocks(d.V) * 8);
     // split-K partials of the MFMA projections at row counts whose tiles cannot fill the GPU
     splitk_floats = 0;
@@ -122,6 +123,8 @@ struct WorkLayout {
     rowmeta = p; p = align256(p + (2 * R + (size_t)d.B) * 4);
     seqtab = p; p = align256(p + (size_t)d.B * sizeof(SeqDesc));
     last = p; p = align256(p + (size_t)d.B * d.dim * 4);
+    // counters of the batch-1 decode block, per layer
+    sync = p; p = align256(p + (size_t)d.L * decode_block_sync_ints(d.G) * 4);
     total = p;
   }
 };
@@ -174,7 +177,9 @@ struct llm_model {
   int* rowmeta;          // device: [R] positions, [R] slots, [B] last-row indices (batched prefill)
   SeqDesc* seqtab;       // device: [B] sequence descriptors (batched prefill)
   float* last;           // device: [B][dim] gathered last rows (batched prefill)
+  int* sync;             // device: decode-block counters, decode_block_sync_ints(G) per layer
   bool mfma_prefill;
+  bool decode_block;     // batch-1 decode runs q|k|v, attention and wo as one launch
   hipStream_t cap_stream;
   std::vector<GraphEntry> graphs;
   // kernel timing (llm_set_kernel_timing)
@@ -289,9 +294,10 @@ struct Partials {
   float* attn;
   float* splitk;
   size_t splitk_floats;
+  int* sync;  // decode-block counters of every layer
 };
 
-Partials ws_partials(const llm_model* m) { return Partials{m->attn, m->splitk, m->splitk_floats}; }
+Partials ws_partials(const llm_model* m) { return Partials{m->attn, m->splitk, m->splitk_floats, m->sync}; }
 
 // y = A W^T with epilogue `ep`.  With norm_w, A is the fp32 residual stream and the
 // projection consumes rmsnorm(A) * norm_w: fused into the GEMV, or a separate RMSNorm
@@ -330,6 +336,54 @@ bool run_layer(llm_model* m, int l, int M, const int* row_pos, const int* row_sl
   const llm_config& c = m->cfg;
   const LayerPtrs& L = m->layers[l];
   const int H = c.n_heads, G = c.n_kv_heads, hd = m->hd, dim = c.dim, F = c.ffn_hidden_dim;
+
+  if (!prefill && M == 1 && m->decode_block && row_pos && row_slot) {
+    // q|k|v, attention and wo of the single decode row in one launch
+    DecodeBlockParams dp;
+    std::memset(&dp, 0, sizeof(dp));
+    dp.x = m->x;
+    dp.attn_norm = L.attn_norm;
+    dp.wqkv = (const _Float16*)L.wqkv;
+    dp.wo = (const _Float16*)L.wo;
+    dp.q = (_Float16*)m->q;
+    dp.o = (_Float16*)m->o;
+    dp.kc = (_Float16*)k_section(m, l);
+    dp.vc = (_Float16*)v_section(m, l);
+    dp.rope_cos = m->rope_cos;
+    dp.rope_sin = m->rope_sin;
+    dp.row_pos = row_pos;
+    dp.row_slot = row_slot;
+    dp.partial = pt.attn;
+    dp.sync = pt.sync + (size_t)l * decode_block_sync_ints(G);
+    dp.err = m->flags;
+    dp.eps = c.norm_eps;
+    dp.dim = dim;
+    dp.H = H;
+    dp.G = G;
+    dp.max_seq = c.max_seq_len;
+    dp.n_slots = c.max_batch;
+    {
+      Timed t(m, LLM_K_DECODE_BLOCK, s);
+      launch_decode_block(dp, s);
+    }
+    EpiParams g = base_epi(m);
+    g.kind = EPI_SWIGLU;
+    g.out_act = m->u;
+    g.ld = F;
+    {
+      Timed t(m, LLM_K_GATE_UP, s);
+      project(m, m->x, L.w13, M, 2 * F, dim, g, s, pt, L.ffn_norm);
+    }
+    EpiParams r = base_epi(m);
+    r.kind = EPI_RESID;
+    r.out_f32 = m->x;
+    r.ld = dim;
+    {
+      Timed t(m, LLM_K_DOWN, s);
+      project(m, m->u, L.w2, M, dim, F, r, s, pt);
+    }
+    return false;
+  }
 
   EpiParams e = base_epi(m);
   e.kind = EPI_QKV;
@@ -431,10 +485,16 @@ hipError_t noalloc_scratch_ptr(void** out) {
 
 // Partial floats a decode step of `batch` rows needs: the attention chunks its launcher picks,
 // and the largest split-K slice set of its projections (the bound launch_gemm_f16 plans with).
-void decode_partials_need(const llm_model* m, int batch, size_t* attn_floats, size_t* splitk_floats) {
+void decode_partials_need(const llm_model* m, int batch, size_t* attn_floats, size_t* splitk_floats,
+                          size_t* sync_ints) {
   const llm_config& c = m->cfg;
   const int hd = m->hd, H = c.n_heads, G = c.n_kv_heads;
   *attn_floats = attn_decode_partial_floats_used(c.dtype, batch, H, G, hd, c.max_seq_len);
+  *sync_ints = 0;
+  if (batch == 1 && m->decode_block) {
+    *attn_floats = std::max(*attn_floats, decode_block_partial_floats(H, c.max_seq_len));
+    *sync_ints = (size_t)c.n_layers * decode_block_sync_ints(G);
+  }
   size_t sk = 0;
   if (use_mfma(m, batch)) {
     const int shapes[5][2] = {{(H + 2 * G) * hd, c.dim}, {c.dim, H * hd}, {2 * c.ffn_hidden_dim, c.dim},
@@ -465,8 +525,11 @@ void enqueue_decode(llm_model* m, int batch, const int* slots, const int* positi
                     hipStream_t s, const Partials& pt) {
   const llm_config& c = m->cfg;
   {
+    // the embedding kernel also clears the decode block's counters of every layer
     Timed t(m, LLM_K_EMBED, s);
-    launch_embed(c.dtype, m->emb, tokens, batch, c.dim, c.vocab_size, m->x, m->flags, s);
+    const bool blk = batch == 1 && m->decode_block;
+    launch_embed(c.dtype, m->emb, tokens, batch, c.dim, c.vocab_size, m->x, m->flags, s, blk ? pt.sync : nullptr,
+                 blk ? c.n_layers * decode_block_sync_ints(c.n_kv_heads) / DB_SYNC_LINE : 0, DB_SYNC_LINE);
   }
   run_layers(m, batch, positions, slots, 0, 0, false, s, pt);
   lm_head(m, m->x, batch, logits, s, pt);
@@ -548,6 +611,8 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   m->rowmeta = (int*)(ws + wl.rowmeta);
   m->seqtab = (SeqDesc*)(ws + wl.seqtab);
   m->last = (float*)(ws + wl.last);
+  m->sync = (int*)(ws + wl.sync);
+  m->decode_block = decode_block_supported(c.dtype, c.dim, c.n_heads, c.n_kv_heads);
   m->mfma_prefill = c.dtype == LLM_BF16 && attn_prefill_supported(d.hd, d.H, d.G);
   m->cap_stream = nullptr;
 
@@ -743,10 +808,11 @@ llm_status llm_decode_step_noalloc(llm_model* m, int32_t batch, const int32_t* s
     return fail(LLM_ERR_INVALID_ARG, "NULL model or buffer");
   if (batch < 1) return fail(LLM_ERR_INVALID_ARG, "batch must be >= 1");
   if (batch > m->cfg.max_batch) return fail(LLM_ERR_OUT_OF_RANGE, "batch > max_batch");
-  size_t attn_f = 0, splitk_f = 0;
-  decode_partials_need(m, batch, &attn_f, &splitk_f);
+  size_t attn_f = 0, splitk_f = 0, sync_n = 0;
+  decode_partials_need(m, batch, &attn_f, &splitk_f, &sync_n);
   const size_t attn_bytes = align256(attn_f * sizeof(float));
-  const size_t need = attn_bytes + splitk_f * sizeof(float);
+  const size_t splitk_bytes = align256(splitk_f * sizeof(float));
+  const size_t need = attn_bytes + splitk_bytes + sync_n * sizeof(int);
   if (need > LLM_NOALLOC_SCRATCH_BYTES)
     return fail(LLM_ERR_OUT_OF_RANGE, "a decode step of " + std::to_string(batch) + " rows needs " +
                                           std::to_string(need) + " bytes of scratch, more than the " +
@@ -755,7 +821,8 @@ llm_status llm_decode_step_noalloc(llm_model* m, int32_t batch, const int32_t* s
   void* base = nullptr;
   const hipError_t e = noalloc_scratch_ptr(&base);
   if (e != hipSuccess) return fail(LLM_ERR_HIP, std::string("static scratch address: ") + hipGetErrorString(e));
-  const Partials pt{(float*)base, (float*)((char*)base + attn_bytes), splitk_f};
+  const Partials pt{(float*)base, (float*)((char*)base + attn_bytes), splitk_f,
+                    (int*)((char*)base + attn_bytes + splitk_bytes)};
   enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, as_stream(stream), pt);
   return hip_check("decode launch");
 }
@@ -864,7 +931,7 @@ void llm_free(llm_model* m) {
 }
 
 const char* llm_status_string(llm_status s) {
-  switch (s) {
+  switch ((int)s) {
     case LLM_OK: return "ok";
     case LLM_ERR_INVALID_ARG: return "invalid argument";
     case LLM_ERR_CONFIG: return "invalid configuration";
