@@ -46,6 +46,7 @@ constexpr int DB_CH = 4 * DB_STEP;      // keys per attention workgroup
 constexpr int DB_VLD = DB_D + 16;       // wave V tile row stride (elements)
 constexpr int DB_VT = DB_STEP * DB_VLD; // one wave's V tile (elements)
 constexpr unsigned DB_SPIN_LIMIT = 1u << 22;
+constexpr int DB_MERGE = 8;             // chunk partials per batch of loads in the merge
 constexpr int DB_SMEM = 4 * DB_VT * 2 + 2 * 4 * DB_MAXH * 4 + 64;
 constexpr float DB_LOG2E = 1.4426950408889634f;
 
@@ -438,20 +439,33 @@ __device__ __forceinline__ void attn_role(const DecodeBlockParams& p, int a, cha
               nvalid - 1;
   __syncthreads();
   if (!*s_last) return;
+  // The partials are read DB_MERGE chunks at a time, all loads of a batch issued before any is
+  // used (device-scope loads go past the L2, so a load-use chain per chunk would cost one
+  // memory round trip per chunk).  Indices past the last chunk are clamped and skipped.
   for (int i = tid; i < npairs; i += 256) {
     const int hh = i / (D / 2), e = 2 * (i % (D / 2));
     const float* pr = p.partial + (size_t)(h0 + hh) * p.nch * (D + 2);
     float m = -1e30f, l = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int c = 0; c < nvalid; ++c) {
-      const float* pc = pr + (size_t)c * (D + 2);
-      const float mc = ld_devf(pc + D), lc = ld_devf(pc + D + 1);
-      const float ac0 = ld_devf(pc + e), ac1 = ld_devf(pc + e + 1);
-      const float mn = fmaxf(m, mc);
-      const float s0 = exp2f(m - mn), s1 = exp2f(mc - mn);
-      l = l * s0 + lc * s1;
-      a0 = a0 * s0 + ac0 * s1;
-      a1 = a1 * s0 + ac1 * s1;
-      m = mn;
+    for (int c0 = 0; c0 < nvalid; c0 += DB_MERGE) {
+      float mc[DB_MERGE], lc[DB_MERGE], ac0[DB_MERGE], ac1[DB_MERGE];
+#pragma unroll
+      for (int j = 0; j < DB_MERGE; ++j) {
+        const float* pc = pr + (size_t)min(c0 + j, nvalid - 1) * (D + 2);
+        mc[j] = ld_devf(pc + D);
+        lc[j] = ld_devf(pc + D + 1);
+        ac0[j] = ld_devf(pc + e);
+        ac1[j] = ld_devf(pc + e + 1);
+      }
+#pragma unroll
+      for (int j = 0; j < DB_MERGE; ++j) {
+        if (c0 + j >= nvalid) break;
+        const float mn = fmaxf(m, mc[j]);
+        const float s0 = exp2f(m - mn), s1 = exp2f(mc[j] - mn);
+        l = l * s0 + lc[j] * s1;
+        a0 = a0 * s0 + ac0[j] * s1;
+        a1 = a1 * s0 + ac1[j] * s1;
+        m = mn;
+      }
     }
     st_dev(p.o + (size_t)(h0 + hh) * D + e, pack2(a0 / l, a1 / l));
   }

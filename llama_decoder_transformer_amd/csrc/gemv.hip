@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(const void* __restrict__ Ain,
 }
 
 // fp16 weights (the bf16-weight path): the same scheme with the weights kept as
-// raw 16-byte words until use, so two chunks x R rows of loads (2R per lane) are
+// raw 16-byte words until use, so U chunks x R rows of loads (U R per lane) are
 // issued before any math.  The products use the packed fp16 dot instruction (two
 // products per lane per instruction, fp32 accumulation) on fp16 activations.
 //
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(const void* __restrict__ Ain,
 // rounds its output, so a large residual cannot overflow fp16 before it is scaled
 // down.  A normalised value outside fp16's range raises LLM_DEVERR_RANGE.
 
-template <int MR, int R, int EPI, bool NORM>
+template <int MR, int R, int EPI, bool NORM, int U>
 __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ain, const f16_t* __restrict__ W,
                                                         const float* __restrict__ gnorm, float eps, int M, int N,
                                                         int K, EpiParams ep) {
@@ -175,15 +175,17 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[i][r] = 0.f;
   const int nchunks = (K + KW - 1) / KW;
-  int kk[2];
-  bool ok[2];
-  u32x4_t wraw[2][R];
+  // Wave w takes chunks w, w + 4, ..., w + 4 (U - 1) of 512 elements per round (U chunks x R
+  // rows of weights in flight per lane).
+  int kk[U];
+  bool ok[U];
+  u32x4_t wraw[U][R];
   // Every load below is unconditional, from an address clamped into the row (K % 8 == 0), and
   // a chunk past the row's end is skipped at use: with no load under a branch the compiler
   // counts the loads in flight exactly and waits only for the ones it needs.
   auto load_w = [&](int c0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < U; ++u) {
       kk[u] = (c0 + 4 * u) * KW + lane * 8;
       ok[u] = kk[u] < K;
       const int kc = min(kk[u], K - 8);
@@ -196,12 +198,12 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   // With the norm: this lane's residual values of the first iteration's two chunks are loaded
   // first (the loop's element mapping, kept in registers for it), then the weights.  Loads
   // complete in issue order, so the statistics below wait for x only, not for the weights.
-  float xa[NORM ? MR : 1][2][8];
+  float xa[NORM ? MR : 1][NORM ? U : 1][8];
   if (NORM) {
 #pragma unroll
     for (int i = 0; i < MR; ++i)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int k = min((wid + 4 * u) * KW + lane * 8, K - 8);
         load8(xin + (size_t)(m0 + min(i, mrows - 1)) * K + k, xa[i][u]);
       }
@@ -216,14 +218,14 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
     for (int i = 0; i < MR; ++i) {
       ss[i] = 0.f;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < U; ++u) {
         if ((wid + 4 * u) * KW + lane * 8 >= K) continue;  // clamped duplicate of another chunk
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss[i] = fmaf(xa[i][u][e], xa[i][u][e], ss[i]);
       }
-      // rows longer than one iteration (K > 4096): the rest of this lane's chunks
+      // rows longer than one round: the rest of this lane's chunks
       if (i < mrows) {
-        for (int c = wid + 8; c < nchunks; c += 4) {
+        for (int c = wid + 4 * U; c < nchunks; c += 4) {
           const int k = c * KW + lane * 8;
           if (k < K) {
             float a[8];
@@ -247,11 +249,11 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
     }
   }
 
-  for (int c0 = wid; c0 < nchunks; c0 += 8) {
+  for (int c0 = wid; c0 < nchunks; c0 += 4 * U) {
     const bool first = c0 == wid;
     if (!first) load_w(c0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (!ok[u]) continue;
       float g[8];
       if (NORM) load8(gnorm + kk[u], g);
@@ -327,17 +329,21 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   raise_range_error(ep, range_bad);
 }
 
-template <int MR, int R, bool NORM>
+template <int MR, int R, bool NORM, int U = 2>
 static void gemv_h_dispatch(const void* A, const f16_t* W, const float* g, float eps, int M, int N, int K,
                                const EpiParams& ep, hipStream_t s) {
   dim3 grid((N + R - 1) / R, (M + MR - 1) / MR);
   switch (ep.kind) {
     case EPI_STORE_F32:
-      launch_k(gemv_h_kernel<MR, R, EPI_STORE_F32, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep);
+      launch_k(gemv_h_kernel<MR, R, EPI_STORE_F32, NORM, U>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep);
       break;
-    case EPI_RESID: launch_k(gemv_h_kernel<MR, R, EPI_RESID, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep); break;
-    case EPI_QKV: launch_k(gemv_h_kernel<MR, R, EPI_QKV, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep); break;
-    case EPI_SWIGLU: launch_k(gemv_h_kernel<MR, R, EPI_SWIGLU, NORM>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep); break;
+    case EPI_RESID:
+      launch_k(gemv_h_kernel<MR, R, EPI_RESID, NORM, U>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep);
+      break;
+    case EPI_QKV: launch_k(gemv_h_kernel<MR, R, EPI_QKV, NORM, U>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep); break;
+    case EPI_SWIGLU:
+      launch_k(gemv_h_kernel<MR, R, EPI_SWIGLU, NORM, U>, grid, 256, 0, s, A, W, g, eps, M, N, K, ep);
+      break;
   }
 }
 
@@ -359,11 +365,12 @@ template <bool NORM>
 static void gemv_h_pick(const void* A, const f16_t* W, const float* g, float eps, int M, int N, int K,
                            const EpiParams& ep, hipStream_t s) {
   // Rows per block for M = 1, from a sweep of the Llama-3-8B projection shapes on MI355X:
-  // LM head (N >= 64K) 16, gate-up (N >= 16K) 8, long-K down projection 2, q|k|v 8, wo 2.
+  // LM head (N >= 64K) 16, gate-up (N >= 16K) 8, long-K down projection 2 (with 4 chunks per
+  // round: 20.4 us against 20.9 with 2 and 22.0 with the whole row, 7, at once), q|k|v 8, wo 2.
   if (M == 1) {
     if (N >= 65536) gemv_h_dispatch<1, 16, NORM>(A, W, g, eps, M, N, K, ep, s);
     else if (N >= 16384) gemv_h_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s);
-    else if (K >= 8192) gemv_h_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+    else if (K >= 8192) gemv_h_dispatch<1, 2, NORM, 4>(A, W, g, eps, M, N, K, ep, s);
     else if (N >= 6144) gemv_h_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s);
     else gemv_h_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
   } else if (M <= 4) {
