@@ -544,7 +544,8 @@ __device__ __forceinline__ int d64_off(int r, int c) { return r * D64_BK + ((c ^
 // wait becomes a wait for all LDS reads.  Completion is tracked by the callers' explicit
 // vector-memory waits, and one wait state follows the M0 write.  The compiler reserves M0 and
 // need not honour it on a clobber list, so this is for kernels in which nothing else uses M0:
-// gemm_dma64_kernel's code has no other M0 access (checked in its ISA).
+// gemm_dma64_kernel's code has no other M0 access.  tests/test_isa_m0.py compiles the sources and
+// fails if the compiler ever emits an M0 access of its own in a function that holds this asm.
 __device__ __forceinline__ void dma16_asm(const f16_t* base, unsigned byte_off, const f16_t* lds) {
   const unsigned lds_addr =
       __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const void __attribute__((address_space(3)))*)lds);
