@@ -235,15 +235,18 @@ llm_status llm_decode_step(llm_model* m, int32_t batch, const int32_t* slots_dev
  * llm_decode_step for callers that cannot allocate device memory at all (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * step and the same results, with the kernels' scratch (the split-KV attention chunk
- * partials and the split-K projection partials) in a static device array of the library
+ * partials, the split-K projection partials, and the batch-1 decode block's partials
+ * and counters) in a static device array of the library
  * instead of regions of the model's workspace.  That array holds 32 MiB on each GPU the
  * library runs on, until the process ends; a step whose partials need more (the
  * message states how much) is rejected with LLM_ERR_OUT_OF_RANGE before anything is
  * enqueued.  (A Llama-3-8B-shaped step of 64 rows over an 8193-position cache needs
  * about 14 MB.)  The call enqueues kernels only: no allocation, no synchronisation.
- * Every call on one GPU shares that GPU's array, and no value in it needs to start at
- * zero (each partial is written before it is read); calls that overlap on one GPU, from
- * several streams or threads, race on it.  Arguments and errors as llm_decode_step.
+ * Every call on one GPU shares that GPU's array and finds there what the last call left:
+ * each partial is written before it is read, and the batch-1 decode's cross-workgroup
+ * counters, the only values that must start at zero, are cleared by the step's first
+ * kernel.  Calls that overlap on one GPU, from several streams or threads, race on it.
+ * Arguments and errors as llm_decode_step.
  */
 llm_status llm_decode_step_noalloc(llm_model* m, int32_t batch, const int32_t* slots_dev,
                                    const int32_t* positions_dev, const int32_t* tokens_dev,
