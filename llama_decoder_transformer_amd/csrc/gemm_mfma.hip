@@ -709,13 +709,15 @@ static int gemm_dma64_dispatch(const f16_t* A, const f16_t* W, int M, int N, int
   const dim3 grid(tm * tn, (nkb + kb_per - 1) / kb_per);
   const int nt = 64 * WGM * WGN;
   constexpr size_t lds = (size_t)2 * (BM + BN) * D64_BK * sizeof(f16_t);
+  // the q|k|v epilogue stages the tile's RoPE rows (BM x d floats, d <= 128) in the same LDS
+  constexpr size_t lds_qkv = std::max(lds, (size_t)BM * 128 * sizeof(float));
   static const bool attr = [] {
     (void)hipFuncSetAttribute((const void*)gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_STORE_F32>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipFuncSetAttribute((const void*)gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_RESID>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipFuncSetAttribute((const void*)gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_QKV>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_qkv);
     (void)hipFuncSetAttribute((const void*)gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_SWIGLU>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     return true;
@@ -729,11 +731,7 @@ static int gemm_dma64_dispatch(const f16_t* A, const f16_t* W, int M, int N, int
       launch_k(gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_RESID>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_QKV:
-      // The staged RoPE rows (BM x d floats, d <= 128) fit square tiles only.
-      if constexpr (BM == BN)
-        launch_k(gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_QKV>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
-      else
-        gemm_dispatch<128, 128, 2, 2>(A, W, M, N, K, ep, s);
+      launch_k(gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_QKV>, grid, nt, lds_qkv, s, A, W, M, N, K, tm, tn, ep, kb_per);
       break;
     case EPI_SWIGLU:
       launch_k(gemm_dma64_kernel<BM, BN, WGM, WGN, EPI_SWIGLU>, grid, nt, lds, s, A, W, M, N, K, tm, tn, ep, kb_per);
@@ -1163,6 +1161,34 @@ size_t gemm_splitk_floats(int M, int N, int K) {
   return need;
 }
 
+// Compute units of the current device (read once; 256 on MI355X).
+static int gemm_cu_count() {
+  static const int n = [] {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipGetLastError();
+    return c > 0 ? c : 256;
+  }();
+  return n;
+}
+
+// 256 x 256 tiles that do not come in whole waves over the CUs leave the last wave partly idle: at
+// M = 2048 the gate-up projection has 896 tiles, 3.5 waves on 256 CUs, so it takes 4 tile times.
+// Then the columns of the whole waves stay on 256 x 256 tiles and the rest go to a second launch
+// on 256 x 128 tiles, when those make at most one wave (at M = 2048: 768 + 256 tiles).  Returns the
+// first column of that tail, or N for no split.
+static int big_tile_tail_split(int M, int N) {
+  const long cus = gemm_cu_count();
+  if (N % 256 != 0) return N;
+  const long tm = (M + 255) / 256, tn = N / 256, t = tm * tn;
+  if (t < cus || t % cus == 0) return N;
+  const long full = t / cus * cus;
+  if (full % tm != 0) return N;
+  const long n_main = full / tm;
+  if (tm * (tn - n_main) * 2 > cus) return N;
+  return (int)(n_main * 256);
+}
+
 // Tile choice from sweeps of the Llama-3-8B projection shapes at M = 16 .. 8192 on MI355X.
 // 8 < M <= 64 with K % 128 == 0 streams the weights through gemm_stream_kernel (stream_plan).
 // Other shapes with K % 32 == 0 use the LDS-DMA kernel: M <= 128 split over K on 64 x 64 tiles
@@ -1257,8 +1283,24 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
   if (M > 64 && K % DS_BK == 0 && (!qkv || dma_qkv_ok)) {
     // The big tiles take 64-wide stages when K allows (whole cache lines per DMA row).
     if (M > 128 && tiles(256, 256) >= 192) {
-      if (dma64_ok(M, N, K)) gemm_dma64_dispatch<256, 256, 2, 4>(a, w, M, N, K, ep, s);
-      else gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
+      // 256 x 192 tiles when they fill the CUs in fewer tile-widths of waves (q|k|v at M = 2048:
+      // 256 tiles, one wave, against 192 of 256 x 256 that leave a quarter of the CUs idle)
+      const long cus = gemm_cu_count();
+      auto wave_cost = [&](int bn) { return (tiles(256, bn) + cus - 1) / cus * bn; };
+      if (dma64_ok(M, N, K) && N % 192 == 0 && wave_cost(192) < wave_cost(256)) {
+        gemm_dma64_dispatch<256, 192, 2, 4>(a, w, M, N, K, ep, s);
+      } else if (dma64_ok(M, N, K)) {
+        // the SwiGLU projection's tail columns (output column = weight row / 2) on narrower tiles
+        const int nt = ep.kind == EPI_SWIGLU ? big_tile_tail_split(M, N) : N;
+        gemm_dma64_dispatch<256, 256, 2, 4>(a, w, M, nt, K, ep, s);
+        if (nt < N) {
+          EpiParams et = ep;
+          et.out_act = (f16_t*)ep.out_act + nt / 2;
+          gemm_dma64_dispatch<256, 128, 4, 2>(a, w + (size_t)nt * K, M, N - nt, K, et, s);
+        }
+      } else {
+        gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
+      }
     } else if (M > 128 && !qkv && tiles(256, 128) >= 192) {
       if (dma64_ok(M, N, K)) gemm_dma64_dispatch<256, 128, 4, 2>(a, w, M, N, K, ep, s);
       else gemm_dma_dispatch<256, 128, 4, 2, 4, true>(a, w, M, N, K, ep, s);
