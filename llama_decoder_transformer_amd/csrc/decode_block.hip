@@ -502,6 +502,10 @@ __device__ __forceinline__ void wo_role(const DecodeBlockParams& p, int w, char*
   const int t = threadIdx.x;
   float resid = 0.f;
   if (t < OR && n0 + t < N) resid = p.x[n0 + t];
+  // Hold the weight stream back a little (wo_delay x 2048 cycles): these workgroups start as q|k|v
+  // workgroups retire, and weight loads issued at once would compete with the last q|k|v loads the
+  // attention waits for; a few microseconds later they fall into the attention's wait instead.
+  for (int i = 0; i < p.wo_delay; ++i) __builtin_amdgcn_s_sleep(32);
   load_w(min(wid, nchunks - 1));
 
   wait_count(p.sync + 2 * p.G * DB_SYNC_LINE, p.G, p.err);
@@ -599,6 +603,10 @@ void launch_decode_block(DecodeBlockParams p, hipStream_t s) {
   p.qkv_per_group = (p.H / p.G + 2) * D / DB_QR;
   const int nw = (p.dim + DB_OR - 1) / DB_OR;
   const DbGeometry& geo = db_geometry();
+  // wo's weight-stream delay, measured at the Llama-3-8B shape (768 q|k|v workgroups, 256 CUs):
+  // 25.1 us per block without, 23.5 / 23.7 / 24.0 us with 3 / 4 / 5 units.  Only q|k|v streams of
+  // at least two workgroups per CU run long enough for it to pay.
+  p.wo_delay = p.nq >= 2 * geo.cus ? 3 : 0;
   // (at least 2: one workgroup per CU would need more LDS than a launch may take by default)
   const int per_cu = std::max(2, std::min(4, (p.nq + geo.cus - 1) / geo.cus));
   // the smallest LDS size at which per_cu + 1 workgroups no longer fit, in 256-byte units

@@ -152,7 +152,7 @@ struct DecodeBlockParams {
   int* err;
   float eps;
   int dim, H, G, max_seq, n_slots;
-  int nq, na, nch, qkv_per_group;  // set by the launcher
+  int nq, na, nch, qkv_per_group, wo_delay;  // set by the launcher
 };
 bool decode_block_supported(int dtype, int dim, int n_heads, int n_kv_heads);
 int decode_block_sync_ints(int n_kv_heads);
