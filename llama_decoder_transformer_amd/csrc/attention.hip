@@ -392,10 +392,11 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 // ============================================================== MFMA prefill
 //
 // fp16 operands, fp32 accumulation and softmax, head_dim 128.  Grid (query block, kv-head x head-block).  A workgroup
-// holds 4 or 8 waves; each wave owns 32 queries of one query head, and the waves of
-// a workgroup share one KV head so a K/V tile of 64 keys is staged in LDS once
-// for all of them (GQA packing: 4 query heads x 32 or 64 queries when the group has 4
-// or more heads).  Heaviest causal blocks are scheduled first.
+// holds 4 waves; each wave owns 32 queries of one query head, and the waves of a workgroup
+// share one KV head so a K/V tile of 64 keys is staged in LDS once for all of them (GQA
+// packing: 4 query heads x 32 queries when the group has 4 or more heads).  For one sequence
+// the work order is folded (heaviest blocks first in the first half of the grid, lightest
+// first in the second), so the two workgroups a CU holds carry an even causal load.
 //
 // Per 64-key tile a wave computes S^T = K Q^T (keys as MFMA rows, queries as
 // columns), so each lane's accumulators all belong to one query column and the
@@ -467,7 +468,19 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
   const int nhb = hpg / HPW;
   const int ld_q = H * PF_D;
   int qblk = gridDim.x - 1 - blockIdx.x;
+  int ycol = blockIdx.y;
   int slot = slot_arg, pos0 = pos0_arg, S = S_arg;
+  if (!seqs) {
+    // One sequence: workgroup id (dispatch order) -> (query block, KV-head column) so that the
+    // column is id % columns (with 8 KV heads each XCD then holds one head's K/V in its L2) and
+    // the query blocks come heaviest first for the first half of the ids and lightest first for
+    // the second: a CU that takes ids i and i + half gets blocks n - 1 - r and r, an even load.
+    const int ny = gridDim.y, nb = gridDim.x;
+    const int id = blockIdx.x + nb * blockIdx.y;
+    ycol = id % ny;
+    const int rank = id / ny, half = (nb + 1) >> 1;
+    qblk = rank < half ? nb - 1 - rank : rank - half;
+  }
   if (seqs) {
     int lo = 0, hi = nseq - 1;
     while (lo < hi) {
@@ -483,8 +496,8 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
     q += (size_t)sd.row0 * ld_q;
     out += (size_t)sd.row0 * ld_q;
   }
-  const int g = blockIdx.y / nhb;
-  const int head = g * hpg + (blockIdx.y % nhb) * HPW + (wid % HPW);
+  const int g = ycol / nhb;
+  const int head = g * hpg + (ycol % nhb) * HPW + (wid % HPW);
   const int qw0 = qblk * QB + 32 * (wid / HPW);
   const int wg_last = min(S, qblk * QB + QB) - 1;
   const int kv_end = pos0 + wg_last + 1;
@@ -906,40 +919,37 @@ static void attn_prefill_launch(dim3 grid, hipStream_t s, const f16_t* q, const 
            out, seqs, nseq);
 }
 
-// Waves per workgroup: nw / hpw sub-blocks of 32 queries share each K/V tile.  8 waves halve
-// the tile fills per query but make each causal block heavier; measured on MI355X at the
-// Llama-3-8B shape: S = 2048 attention 85-88 us with 8 waves against 95 with 4, S = 8192 836
-// against 739-767.
-static int attn_prefill_waves(int max_n) { return max_n <= 4096 ? 8 : 4; }
+// Waves per workgroup: 4 / hpw sub-blocks of 32 queries share each K/V tile.  With the folded
+// work order of a single sequence (two workgroups per CU, a heavy and a light query block) 4 waves
+// beat 8 (one workgroup per CU, each as heavy as its causal block): measured on MI355X at the
+// Llama-3-8B shape, S = 2048 62-66 us against 74-75 with 8 waves, S = 8192 683 us against 763
+// before the fold.
+constexpr int PF_WAVES = 4;
 
 int attn_prefill_block_rows(int max_n, int n_heads, int n_kv_heads) {
+  (void)max_n;
   const int hpg = n_heads / n_kv_heads;
   const int hpw = hpg >= 4 ? 4 : hpg;
-  return 32 * (attn_prefill_waves(max_n) / hpw);
+  return 32 * (PF_WAVES / hpw);
 }
 
 static void attn_prefill_any(const void* q, const void* k_cache, const void* v_cache, int slot, int pos0,
                              int n_tokens, int max_n, int n_blocks, const SeqDesc* seqs, int nseq, int n_heads,
                              int n_kv_heads, int max_seq, void* out, hipStream_t s) {
+  (void)max_n;
   const int hpg = n_heads / n_kv_heads;
   const int hpw = hpg >= 4 ? 4 : hpg;
-  const int nw = attn_prefill_waves(max_n);
   dim3 grid(n_blocks, n_kv_heads * (hpg / hpw));
   const f16_t* qq = (const f16_t*)q;
   const f16_t* kk = (const f16_t*)k_cache;
   const f16_t* vv = (const f16_t*)v_cache;
   f16_t* oo = (f16_t*)out;
-#define LLM_PF(HPW, NW) \
-  attn_prefill_launch<HPW, NW>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo, seqs, nseq)
-  if (nw == 8) {
-    if (hpw == 4) LLM_PF(4, 8);
-    else if (hpw == 2) LLM_PF(2, 8);
-    else LLM_PF(1, 8);
-  } else {
-    if (hpw == 4) LLM_PF(4, 4);
-    else if (hpw == 2) LLM_PF(2, 4);
-    else LLM_PF(1, 4);
-  }
+#define LLM_PF(HPW) \
+  attn_prefill_launch<HPW, PF_WAVES>(grid, s, qq, kk, vv, slot, pos0, n_tokens, n_heads, n_kv_heads, max_seq, oo, \
+                                     seqs, nseq)
+  if (hpw == 4) LLM_PF(4);
+  else if (hpw == 2) LLM_PF(2);
+  else LLM_PF(1);
 #undef LLM_PF
 }
 
