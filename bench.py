@@ -228,6 +228,12 @@ def bench_generate(args, torch, B, inputs, LlamaModel, shared, steps: int, warmu
 
     L, dim, F, V = shape.n_layers, shape.dim, shape.ffn_hidden_dim, shape.vocab_size
     up_bytes = 2 * F * dim * 2 + 2 * dim * 4 + F * 2  # w1|w3 weights + fp32 x and norm weight in + SwiGLU row out
+    hd, H, G = shape.head_dim, shape.n_heads, shape.n_kv_heads
+    # one decode-block launch (q|k|v GEMV + attention + wo GEMV of a layer): the q|k|v and wo weights
+    # (fp16), the layer's cached keys and values at the mean decode context (fp16), x read twice and
+    # written once plus the norm weight (fp32)
+    mean_ctx_blk = P + (T - 1) / 2.0 + 1
+    blk_bytes = 2 * (dim * (H + 2 * G) * hd + H * hd * dim) + G * hd * 2 * 2 * mean_ctx_blk + 4 * dim * 4
     per_kernel = per_kernel_table(kt_prefill, "prefill")
     for k, v in per_kernel_table(kt_decode, "decode").items():
         per_kernel.setdefault(k, {}).update(v)
@@ -249,6 +255,9 @@ def bench_generate(args, torch, B, inputs, LlamaModel, shared, steps: int, warmu
         "decode_step_hbm_frac": round(dec_bytes / (decode_ms / T * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": hbm_roofline("decode gate-up projection (w1|w3 GEMV + fused RMSNorm + SwiGLU), M=1", up_bytes,
                                  avg_ms(kt_decode, "gate_up"), measured_traffic("decode_gate_up_gemv")),
+        "roofline_decode_block": hbm_roofline("decode block: q|k|v GEMV + attention + wo GEMV of one layer, M=1",
+                                              blk_bytes, avg_ms(kt_decode, "decode_block"),
+                                              measured_traffic("decode_block")),
         "roofline_prefill": mfma_roofline("prefill gate-up GEMM (M=512, N=28672, K=4096) + SwiGLU",
                                           2.0 * P * (2 * F) * dim, avg_ms(kt_prefill, "gate_up")),
         "per_kernel": per_kernel,
