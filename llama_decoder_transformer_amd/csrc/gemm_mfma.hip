@@ -1117,12 +1117,14 @@ int gemm_splitk_count(int M, int N, int K) {
 }
 
 // Prefill row counts (M > 128) whose large tiles cannot fill the GPU: 256 x 256 tiles when they
-// number at least 192, else 256 x 128 (not for the q|k|v epilogue, which needs square tiles)
-// when they do; otherwise K is split over the 256 x 256 or 256 x 128 tiles with at least 1024
-// k per slice and at most 320 workgroups, taking the most workgroups up to 256, then the fewest
-// slices, then the larger tile.  From a sweep of the Llama-3-8B projections at M = 256, 512
-// and 1024 on MI355X (e.g. down at M = 512: 498 TFLOP/s unsplit on 64 x 64 tiles, 841 on
-// 256 x 128 tiles in 4 slices, the partial sums included).
+// number at least 192; else, with K >= 4096, 256 x 256 tiles in 2 K slices when that gives 192
+// to 320 workgroups (not for q|k|v); else 256 x 128 (not for q|k|v) when they number at least
+// 192; otherwise K is split over the 256 x 256 or 256 x 128 tiles with at least 1024 k per
+// slice and at most 320 workgroups, taking the most workgroups up to 256, then the fewest
+// slices, then the larger tile.  From sweeps of the Llama-3-8B projections on MI355X: down at
+// M = 512, 498 TFLOP/s unsplit on 64 x 64 tiles, 841 on 256 x 128 tiles in 4 slices; down at
+// M = 2048, 280 us on 256 x 128 tiles against 212 on 256 x 256 tiles in 2 slices and wo 92
+// against 88, the partial sums and their reduction included.
 struct BigPlan {
   int tile;  // 0: 256 x 256, 1: 256 x 128
   int splits;
@@ -1132,6 +1134,10 @@ static bool big_tile_plan(int M, int N, int K, bool qkv, BigPlan& p) {
   if (M <= 128 || K % DS_BK != 0) return false;
   auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (tiles(256, 256) >= 192) { p = {0, 1}; return true; }
+  if (!qkv && K >= 4096 && N % 4 == 0 && tiles(256, 256) * 2 >= 192 && tiles(256, 256) * 2 <= 320) {
+    p = {0, 2};
+    return true;
+  }
   if (!qkv && tiles(256, 128) >= 192) { p = {1, 1}; return true; }
   long best = 0;
   bool found = false;
