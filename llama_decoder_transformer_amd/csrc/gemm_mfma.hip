@@ -1180,9 +1180,9 @@ static int gemm_cu_count() {
 
 // 256 x 256 tiles that do not come in whole waves over the CUs leave the last wave partly idle: at
 // M = 2048 the gate-up projection has 896 tiles, 3.5 waves on 256 CUs, so it takes 4 tile times.
-// Then the columns of the whole waves stay on 256 x 256 tiles and the rest go to a second launch
-// on 256 x 128 tiles, when those make at most one wave (at M = 2048: 768 + 256 tiles).  Returns the
-// first column of that tail, or N for no split.
+// Then the columns of the whole waves stay on 256 x 256 tiles and the rest go to a second GEMM,
+// when that is at most one wave of 256 x 128 tiles (at M = 2048: 768 tiles, then a 4096-column
+// GEMM).  Returns the first column of that tail, or N for no split.
 static int big_tile_tail_split(int M, int N) {
   const long cus = gemm_cu_count();
   if (N % 256 != 0) return N;
@@ -1218,6 +1218,19 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
       case EPI_SWIGLU: launch_k(splitk_reduce_kernel<EPI_SWIGLU>, grid, 256, 0, s, splitk_ws, ns, M, N, ep); break;
     }
   };
+  if (ep.kind == EPI_SWIGLU && M > 128 && dma64_ok(M, N, K) && tiles(256, 256) >= 192) {
+    // The SwiGLU projection's columns beyond its whole waves of 256 x 256 tiles go to a second GEMM,
+    // planned on its own (at M = 2048: 256 x 256 tiles in two K slices); output column = weight
+    // row / 2.
+    const int nt = big_tile_tail_split(M, N);
+    if (nt < N) {
+      launch_gemm_f16(A, W, M, nt, K, ep, splitk_ws, splitk_ws_floats, s);
+      EpiParams et = ep;
+      et.out_act = (f16_t*)ep.out_act + nt / 2;
+      launch_gemm_f16(A, w + (size_t)nt * K, M, N - nt, K, et, splitk_ws, splitk_ws_floats, s);
+      return;
+    }
+  }
   {
     BigPlan bp;
     if (big_tile_plan(M, N, K, ep.kind == EPI_QKV, bp) && bp.splits > 1 && splitk_ws &&
@@ -1296,14 +1309,7 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
       if (dma64_ok(M, N, K) && N % 192 == 0 && wave_cost(192) < wave_cost(256)) {
         gemm_dma64_dispatch<256, 192, 2, 4>(a, w, M, N, K, ep, s);
       } else if (dma64_ok(M, N, K)) {
-        // the SwiGLU projection's tail columns (output column = weight row / 2) on narrower tiles
-        const int nt = ep.kind == EPI_SWIGLU ? big_tile_tail_split(M, N) : N;
-        gemm_dma64_dispatch<256, 256, 2, 4>(a, w, M, nt, K, ep, s);
-        if (nt < N) {
-          EpiParams et = ep;
-          et.out_act = (f16_t*)ep.out_act + nt / 2;
-          gemm_dma64_dispatch<256, 128, 4, 2>(a, w + (size_t)nt * K, M, N - nt, K, et, s);
-        }
+        gemm_dma64_dispatch<256, 256, 2, 4>(a, w, M, N, K, ep, s);
       } else {
         gemm_dma_dispatch<256, 256, 2, 4, 4, true>(a, w, M, N, K, ep, s);
       }
