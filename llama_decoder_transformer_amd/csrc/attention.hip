@@ -408,9 +408,9 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 // heaviest blocks of the last sequence) to the first, and each workgroup finds its
 // sequence by a binary search over the descriptors' first-block indices.
 //
-// K/V tiles are double-buffered in LDS: the next tile's global loads are issued
-// into registers before the current tile's math, stored after it, and a single
-// barrier per tile separates the two buffers' uses.  The causal mask is applied
+// K/V tiles are double-buffered in LDS and arrive by LDS DMA (no registers stage them): the
+// next tile's DMA is issued before the current tile's math, each wave waits for its own DMA
+// after it, and a single barrier per tile separates the two buffers' uses.  The causal mask is applied
 // only on tiles that cross a wave's diagonal, and the running max is raised only
 // when a score exceeds it by more than 2^8 (the accumulators are rescaled then,
 // for the whole wave at once); between raises the probabilities stay below 256,
@@ -418,15 +418,21 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 
 constexpr int PF_D = 128;
 constexpr int PF_KT = 64;
-constexpr int PF_KLD = PF_D + 8;    // K row stride: 272 bytes (b128 fragment reads: 16 rows hit 64 distinct banks)
 constexpr int PF_VLD = PF_D + 16;   // decode V tile row stride: 288 bytes (transposing reads of 8 rows x 32 bytes hit distinct banks)
-// Prefill V tile row stride: 320 bytes.  A 32-lane half of a transposing read covers 4 key rows x
-// 64 bytes; rows 64 bytes (16 banks) apart modulo 256 keep them on distinct banks (at 288 bytes
-// a quarter of the LDS cycles were bank conflicts).
-constexpr int PF_KTILE = PF_KT * PF_KLD;  // elements
-constexpr int PF_VLD2 = PF_D + 32;
-constexpr int PF_VTILE = PF_KT * PF_VLD2;
+// Prefill K and V tiles: 64 unpadded rows of 256 bytes (16 chunks of 16 bytes), filled by LDS DMA
+// (one instruction fills 4 whole rows, lane l taking physical chunk l % 16 of row l / 16), with
+// the chunks permuted per row so that the fragment reads hit distinct banks:
+//  - K, chunk c of row r at c ^ pf_kswz(r).  A 16-byte read is served a pair of lane octets at a
+//    time, (0-7, 16-23), ...; the S^T fragments put rows r and r + 16 of one chunk in such a pair,
+//    so the permutation takes row bits 0-2 and bit 4: 16 distinct chunks, all 64 banks.
+//  - V, chunk c of row r at c ^ pf_vswz(r).  A 32-lane half of a transposing read covers 4
+//    consecutive rows x 4 chunks; XOR-ing row bits 0-1 into chunk bits 2-3 puts the 4 rows on 4
+//    distinct groups of 4 chunks.
+constexpr int PF_KTILE = PF_KT * PF_D;  // elements
+constexpr int PF_VTILE = PF_KT * PF_D;
 constexpr size_t PF_LDS_BYTES = 2 * (size_t)(PF_KTILE + PF_VTILE) * sizeof(f16_t);
+__device__ __forceinline__ int pf_kswz(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
+__device__ __forceinline__ int pf_vswz(int r) { return (r & 3) << 2; }
 constexpr float PF_RESCALE_LOG2 = 8.0f;
 
 typedef short pf_v4i16 __attribute__((ext_vector_type(4)));
@@ -456,8 +462,8 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
   typedef float f32x16_t __attribute__((ext_vector_type(16)));
   constexpr int QSUB = NW / HPW;  // 32-query sub-blocks per workgroup
   constexpr int QB = 32 * QSUB;
-  constexpr int NT = 64 * NW;     // threads
-  constexpr int NL = 1024 / NT;   // 16-byte loads per thread per K (and V) tile
+  constexpr int NI = 16 / NW;     // DMA instructions per wave per K (and V) tile: 4 rows each
+  static_assert(16 % NW == 0, "the 16 four-row blocks of a tile do not split over the waves");
   extern __shared__ __attribute__((aligned(16))) f16_t pf_smem[];
   f16_t* const Ks0 = pf_smem;
   f16_t* const Vs0 = pf_smem + 2 * PF_KTILE;
@@ -530,43 +536,41 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
   const int wave_last_pos = wave_first_pos + 31;
   const int qpos = wave_first_pos + l32;
 
-  u32x4_t kr[NL], vr[NL];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int idx = tid + i * NT, key = idx >> 4, c = idx & 15;
-      kr[i] = u32x4_t{0u, 0u, 0u, 0u};
-      vr[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (k0 + key < kv_end) {
-        kr[i] = *reinterpret_cast<const u32x4_t*>(kb + (size_t)(k0 + key) * PF_D + c * 8);
-        vr[i] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)(k0 + key) * PF_D + c * 8);
-      }
-    }
-  };
-  auto stash = [&](int buf) {
+  // DMA of the tile at key k0 into buffer buf: this wave's 4-row blocks wid * NI .. + NI - 1 of K
+  // and of V.  Rows past kv_end load row kv_end - 1 (finite values; their scores are masked).
+  const int d_row = lane >> 4, d_pc = lane & 15;
+  auto issue = [&](int buf, int k0) __attribute__((always_inline)) {
     f16_t* Ks = Ks0 + buf * PF_KTILE;
     f16_t* Vs = Vs0 + buf * PF_VTILE;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int idx = tid + i * NT, key = idx >> 4, c = idx & 15;
-      *reinterpret_cast<u32x4_t*>(&Ks[key * PF_KLD + c * 8]) = kr[i];
-      *reinterpret_cast<u32x4_t*>(&Vs[key * PF_VLD2 + c * 8]) = vr[i];
+    for (int i = 0; i < NI; ++i) {
+      const int blk = wid * NI + i, r = blk * 4 + d_row;
+      const size_t key = (size_t)min(k0 + r, kv_end - 1);
+      dma16_asm(kb, (unsigned)((key * PF_D + ((d_pc ^ pf_kswz(r)) << 3)) * sizeof(f16_t)), Ks + blk * 4 * PF_D);
+      dma16_asm(vb, (unsigned)((key * PF_D + ((d_pc ^ pf_vswz(r)) << 3)) * sizeof(f16_t)), Vs + blk * 4 * PF_D);
     }
   };
+  auto tile_barrier = [&]() __attribute__((always_inline)) {
+    wait_vmcnt<0>();  // this wave's DMA has landed
+    __syncthreads();  // every wave's has, and every wave is done with the other buffer
+  };
 
-  fetch(0);
-  stash(0);
-  __syncthreads();
+  issue(0, 0);
+  tile_barrier();
 
   // V^T read address of this lane: key row 4 lh + (l % 16) / 4 of a 16-key half, columns
-  // 16 ((l / 16) % 2) + 4 (l % 4) of a 32-dimension block.
+  // 16 ((l / 16) % 2) + 4 (l % 4) of a 32-dimension block, i.e. logical chunk
+  // 2 ((l / 16) % 2) + (l % 4) / 2 + 4 mb of block mb, half (l % 2).  Every row a lane reads is
+  // 4 lh + (l % 16) / 4 modulo 4, so its chunk permutation is the same for all of them.
   const int v_row = 4 * lh + ((lane & 15) >> 2);
-  const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int v_c0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int v_sw = pf_vswz(v_row);
+  const int v_half = 4 * (lane & 1);
 
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * PF_KT;
     const bool more = t + 1 < ntiles;
-    if (more) fetch(k0 + PF_KT);
+    if (more) issue((t + 1) & 1, k0 + PF_KT);
     const f16_t* Ks = Ks0 + (t & 1) * PF_KTILE;
     const f16_t* Vs = Vs0 + (t & 1) * PF_VTILE;
 
@@ -581,7 +585,9 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
       for (int s8 = 0; s8 < 8; ++s8) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const f16x8_t kf = *reinterpret_cast<const f16x8_t*>(&Ks[(kb2 * 32 + l32) * PF_KLD + s8 * 16 + lh * 8]);
+          const int kr = kb2 * 32 + l32;
+          const f16x8_t kf =
+              *reinterpret_cast<const f16x8_t*>(&Ks[kr * PF_D + (((2 * s8 + lh) ^ pf_kswz(kr)) << 3)]);
           st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s8], st[kb2], 0, 0, 0);
         }
       }
@@ -629,19 +635,19 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
       // O^T += V^T P^T
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        const f16_t* vrow = Vs + (16 * t4 + v_row) * PF_VLD2 + v_col;
+        const f16_t* vrow = Vs + (16 * t4 + v_row) * PF_D + v_half;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-          const uint2 lo = pf_read_tr(vrow + 32 * mb);
-          const uint2 hi = pf_read_tr(vrow + 8 * PF_VLD2 + 32 * mb);
+          const int pc = ((v_c0 + 4 * mb) ^ v_sw) << 3;
+          const uint2 lo = pf_read_tr(vrow + pc);
+          const uint2 hi = pf_read_tr(vrow + 8 * PF_D + pc);
           const u32x4_t u = {lo.x, lo.y, hi.x, hi.y};
           o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, u), pf[t4], o[mb], 0, 0, 0);
         }
       }
     }
 
-    if (more) stash((t + 1) & 1);
-    __syncthreads();
+    tile_barrier();
   }
 
   // Normalise and store: lane holds dims 32 mb + (e % 4) + 8 (e / 4) + 4 lh of query l32.

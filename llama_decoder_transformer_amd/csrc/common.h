@@ -101,4 +101,28 @@ __device__ __forceinline__ void load8(const float* p, float* out) {
   for (int i = 0; i < 4; ++i) { out[i] = a[i]; out[4 + i] = b[i]; }
 }
 
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
+template <int V>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(V >= 0 && V < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte-per-lane global -> LDS DMA from base + byte_off (uniform base, per-lane 32-bit
+// offset; lane l's bytes land at lds + 16 l), in asm so that the
+// compiler does not count it among the LDS operations: with the builtin, every later fragment
+// wait becomes a wait for all LDS reads.  Completion is tracked by the callers' explicit
+// vector-memory waits, and one wait state follows the M0 write.  The compiler reserves M0 and
+// need not honour it on a clobber list, so this is for kernels in which nothing else uses M0:
+// the kernels that use it (the 64-wide-stage GEMM, the prefill attention) have no other M0 access.
+// tests/test_isa_m0.py compiles the sources and fails if the compiler ever emits an M0 access of
+// its own in a function that holds this asm.
+__device__ __forceinline__ void dma16_asm(const f16_t* base, unsigned byte_off, const f16_t* lds) {
+  const unsigned lds_addr =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const void __attribute__((address_space(3)))*)lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
+               "s"(lds_addr)
+               : "memory", "m0");
+}
+
 }  // namespace llm

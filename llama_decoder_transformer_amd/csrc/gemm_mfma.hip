@@ -244,12 +244,6 @@ __device__ __forceinline__ void dma_tile_of(int id, int tiles_m, int tiles_n, in
 
 __device__ __forceinline__ int ds_off(int r, int c) { return r * DS_BK + ((c ^ ((r >> 1) & 3)) << 3); }
 
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
-template <int V>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(V >= 0 && V < 64, "vmcnt out of range");
-  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Epilogue of the DMA kernels: the wave's FM x FN accumulator blocks cover rows m0.. and columns
 // n0.. of the BM-row tile starting at row tm; smem holds at least BM x d floats for the RoPE rows.
@@ -537,22 +531,6 @@ static int gemm_dma_dispatch(const f16_t* A, const f16_t* W, int M, int N, int K
 constexpr int D64_BK = 64;
 
 __device__ __forceinline__ int d64_off(int r, int c) { return r * D64_BK + ((c ^ (r & 7)) << 3); }
-
-// One 16-byte-per-lane global -> LDS DMA from base + byte_off (uniform base, per-lane 32-bit
-// offset; lane l's bytes land at lds + 16 l), in asm so that the
-// compiler does not count it among the LDS operations: with the builtin, every later fragment
-// wait becomes a wait for all LDS reads.  Completion is tracked by the callers' explicit
-// vector-memory waits, and one wait state follows the M0 write.  The compiler reserves M0 and
-// need not honour it on a clobber list, so this is for kernels in which nothing else uses M0:
-// gemm_dma64_kernel's code has no other M0 access.  tests/test_isa_m0.py compiles the sources and
-// fails if the compiler ever emits an M0 access of its own in a function that holds this asm.
-__device__ __forceinline__ void dma16_asm(const f16_t* base, unsigned byte_off, const f16_t* lds) {
-  const unsigned lds_addr =
-      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const void __attribute__((address_space(3)))*)lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
-               "s"(lds_addr)
-               : "memory", "m0");
-}
 
 template <int BM, int BN, int WGM, int WGN, int EPI>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma64_kernel(const f16_t* __restrict__ A,
