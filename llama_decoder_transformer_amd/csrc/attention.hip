@@ -700,7 +700,8 @@ attn_decode_mfma_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ k
 
   const int chunk = blockIdx.x, g = blockIdx.y, row = blockIdx.z;
   const int hpg = H / G, h0 = g * hpg;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the step loop branches on scalars
   const int l16 = lane & 15, lg = lane >> 4;
   const int pos = row_pos ? row_pos[row] : pos0 + row;
   const int slot = row_slot ? row_slot[row] : slot0;
@@ -743,24 +744,23 @@ attn_decode_mfma_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ k
   float mrow = -1e30f, lrow = 0.f;
 
   // Raw rows of one step: K as MFMA A operands (key k0 + 16 kb + l16, d = 32 s + 8 lg), V in
-  // copy order (key (lane + 64 i) / 16, 16-byte column (lane + 64 i) % 16).
+  // copy order (key (lane + 64 i) / 16, 16-byte column (lane + 64 i) % 16).  Every load is
+  // unconditional, from a key clamped to wend - 1 (its score is masked and its V row meets a zero
+  // probability): with the loads under a branch the compiler could not count them and waited for
+  // the next step's loads too (vmcnt(0)) before each step, which undid the prefetch.
   u32x4_t kr[2][2][4], vr[2][8];
   auto fetch = [&](int set, int k0) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int key = k0 + kb2 * 16 + l16;
-      const bool ok = key < wend;
+      const int key = min(k0 + kb2 * 16 + l16, wend - 1);
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        kr[set][kb2][s4] = u32x4_t{0u, 0u, 0u, 0u};
-        if (ok) kr[set][kb2][s4] = *reinterpret_cast<const u32x4_t*>(kb + (size_t)key * D + s4 * 32 + lg * 8);
-      }
+      for (int s4 = 0; s4 < 4; ++s4)
+        kr[set][kb2][s4] = *reinterpret_cast<const u32x4_t*>(kb + (size_t)key * D + s4 * 32 + lg * 8);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int idx = lane + 64 * i, key = k0 + (idx >> 4), c = idx & 15;
-      vr[set][i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (key < wend) vr[set][i] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)key * D + c * 8);
+      const int idx = lane + 64 * i, key = min(k0 + (idx >> 4), wend - 1), c = idx & 15;
+      vr[set][i] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)key * D + c * 8);
     }
   };
 
@@ -823,13 +823,15 @@ attn_decode_mfma_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ k
     }
   };
 
+  // The next step's rows are always fetched (past the last step they are clamped copies of row
+  // wend - 1 and go unused), so no load sits under a branch.
   if (nsteps > 0) fetch(0, wbeg);
   for (int i = 0; i < nsteps; i += 2) {
     const int k0 = wbeg + i * DM_STEP;
-    if (i + 1 < nsteps) fetch(1, k0 + DM_STEP);
+    fetch(1, k0 + DM_STEP);
     step(0, k0);
     if (i + 1 >= nsteps) break;
-    if (i + 2 < nsteps) fetch(0, k0 + 2 * DM_STEP);
+    fetch(0, k0 + 2 * DM_STEP);
     step(1, k0 + DM_STEP);
   }
 
