@@ -61,10 +61,24 @@ __device__ __forceinline__ void st_dev(void* p, uint32_t v) {
 __device__ __forceinline__ uint32_t ld_dev(const void* p) {
   return __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_devf(const float* p) { return __uint_as_float(ld_dev(p)); }
+// 64-bit device-scope loads (8-byte aligned addresses): measured on MI355X, a GEMV-shaped launch
+// in which every workgroup also reads a shared 28 KB vector this way took 24.4 us against 22.7
+// with plain loads, and 30.6 with 32-bit device-scope loads.
+__device__ __forceinline__ uint64_t ld_dev64(const void* p) {
+  return __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev64(void* p, float lo, float hi) {
+  const uint64_t v = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ld_dev2f(const float* p, float& lo, float& hi) {
+  const uint64_t v = ld_dev64(p);
+  lo = __uint_as_float((uint32_t)v);
+  hi = __uint_as_float((uint32_t)(v >> 32));
+}
 __device__ __forceinline__ u32x4_t ld_dev4(const void* p) {
-  const uint32_t* q = (const uint32_t*)p;
-  return u32x4_t{ld_dev(q), ld_dev(q + 1), ld_dev(q + 2), ld_dev(q + 3)};
+  const uint64_t a = ld_dev64(p), b = ld_dev64((const char*)p + 8);
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
 }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -84,6 +98,19 @@ __device__ __forceinline__ void signal(int* cnt) {
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// The attention-done counter, which every wo workgroup waits on, is kept in DB_REP copies on
+// consecutive lines, each moved by every signal; a waiter polls copy (its index % DB_REP), so the
+// polls spread over that many lines instead of queueing on one (measured at the Llama-3-8B shape,
+// positions 512..767: with the 64-bit accesses above, 21.9 us per block against 23.4).
+constexpr int DB_REP = 16;
+__device__ __forceinline__ void signal_rep(int* cnt) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x < DB_REP)
+    __hip_atomic_fetch_add(cnt + threadIdx.x * DB_SYNC_LINE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ const int* rep_copy(const int* cnt) { return cnt + (blockIdx.x % DB_REP) * DB_SYNC_LINE; }
 
 // Until *cnt reaches target (thread 0 polls, the workgroup waits at the barrier), bounded.
 __device__ __forceinline__ void wait_count(const int* cnt, int target, int* err) {
@@ -276,7 +303,7 @@ __device__ __forceinline__ void attn_role(const DecodeBlockParams& p, int a, cha
     // no attention for an invalid row: the first chunk of each group writes zeros
     if (chunk == 0) {
       for (int i = tid; i < hpg * D / 2; i += 256) st_dev(p.o + (size_t)h0 * D + 2 * i, 0u);
-      signal(ocnt);
+      signal_rep(ocnt);
     }
     return;
   }
@@ -419,16 +446,13 @@ __device__ __forceinline__ void attn_role(const DecodeBlockParams& p, int a, cha
       st_dev(p.o + (size_t)(h0 + hh) * D + e, pack2(a0 / L, a1 / L));
     } else {
       float* pr = p.partial + ((size_t)(h0 + hh) * p.nch + chunk) * (D + 2);
-      st_dev(pr + e, __float_as_uint(a0));
-      st_dev(pr + e + 1, __float_as_uint(a1));
-      if (e == 0) {
-        st_dev(pr + D, __float_as_uint(M));
-        st_dev(pr + D + 1, __float_as_uint(L));
-      }
+      // a partial is 130 floats (520 bytes), so every pair below is 8-byte aligned
+      st_dev64(pr + e, a0, a1);
+      if (e == 0) st_dev64(pr + D, M, L);
     }
   }
   if (nvalid == 1) {
-    signal(ocnt);
+    signal_rep(ocnt);
     return;
   }
   // the last chunk of the group to arrive merges the partials
@@ -451,10 +475,8 @@ __device__ __forceinline__ void attn_role(const DecodeBlockParams& p, int a, cha
 #pragma unroll
       for (int j = 0; j < DB_MERGE; ++j) {
         const float* pc = pr + (size_t)min(c0 + j, nvalid - 1) * (D + 2);
-        mc[j] = ld_devf(pc + D);
-        lc[j] = ld_devf(pc + D + 1);
-        ac0[j] = ld_devf(pc + e);
-        ac1[j] = ld_devf(pc + e + 1);
+        ld_dev2f(pc + D, mc[j], lc[j]);
+        ld_dev2f(pc + e, ac0[j], ac1[j]);
       }
 #pragma unroll
       for (int j = 0; j < DB_MERGE; ++j) {
@@ -469,7 +491,7 @@ __device__ __forceinline__ void attn_role(const DecodeBlockParams& p, int a, cha
     }
     st_dev(p.o + (size_t)(h0 + hh) * D + e, pack2(a0 / l, a1 / l));
   }
-  signal(ocnt);
+  signal_rep(ocnt);
 }
 
 // ------------------------------------------------------------------ role 3: wo GEMV
@@ -508,7 +530,7 @@ __device__ __forceinline__ void wo_role(const DecodeBlockParams& p, int w, char*
   for (int i = 0; i < p.wo_delay; ++i) __builtin_amdgcn_s_sleep(32);
   load_w(min(wid, nchunks - 1));
 
-  wait_count(p.sync + 2 * p.G * DB_SYNC_LINE, p.G, p.err);
+  wait_count(rep_copy(p.sync + 2 * p.G * DB_SYNC_LINE), p.G, p.err);
 
   float acc[OR];
 #pragma unroll
@@ -564,9 +586,9 @@ bool decode_block_supported(int dtype, int dim, int n_heads, int n_kv_heads) {
   return hd == DB_D && hpg <= DB_MAXH && dim % 8 == 0 && (hd % DB_QR) == 0;
 }
 
-// per layer: G group counters (q|k|v rows done), G chunk counters and the attention-done
-// counter, one 128-byte line each
-int decode_block_sync_ints(int n_kv_heads) { return (2 * n_kv_heads + 1) * DB_SYNC_LINE; }
+// per layer: G group counters (q|k|v rows done), G chunk counters and DB_REP copies of the
+// attention-done counter, one 128-byte line each
+int decode_block_sync_ints(int n_kv_heads) { return (2 * n_kv_heads + DB_REP) * DB_SYNC_LINE; }
 
 // Workgroups per CU.  The q|k|v workgroups should all run at once and alone at first: the wo
 // workgroups (later in dispatch order) then start, and stream their weights, only as q|k|v

@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   };
   const float* const xin = reinterpret_cast<const float*>(Ain);
 
-  // With the norm: this lane's residual values of the first iteration's two chunks are loaded
+  // With the norm: this lane's residual values of the first round's U chunks are loaded
   // first (the loop's element mapping, kept in registers for it), then the weights.  Loads
   // complete in issue order, so the statistics below wait for x only, not for the weights.
   float xa[NORM ? MR : 1][NORM ? U : 1][8];
