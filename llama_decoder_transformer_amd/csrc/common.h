@@ -25,6 +25,18 @@ constexpr int LLM_DEVERR_SYNC_BIT = 16;
 // True when fp16(v) is not finite: |v| rounds past the largest fp16 value (65504) or v is NaN.
 __device__ __forceinline__ bool f16_out_of_range(float v) { return !(__builtin_fabsf(v) < 65520.0f); }
 
+// Greedy-argmax key of logit v at index i: the unsigned order of keys is the order "higher logit,
+// then lower index", the one the argmax kernels use, so the row's argmax is the maximum key (an
+// atomicMax).  The high word maps the float to an order-preserving integer (-0 taken as +0, so
+// that a tie of the two zeros goes to the lower index as a float compare has it), the low word
+// is ~i.  A NaN logit gets key 0 and is never chosen; 0 also means "no key yet".
+__device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
+  if (v != v) return 0ull;
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)o << 32) | (uint32_t)~(uint32_t)i;
+}
+
 // Range check of a value about to be stored in the activation dtype (only fp16 can overflow).
 template <typename T> __device__ __forceinline__ bool store_out_of_range(float v) {
   if constexpr (__is_same(T, f16_t)) return f16_out_of_range(v);

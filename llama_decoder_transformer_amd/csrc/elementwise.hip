@@ -255,6 +255,49 @@ void launch_advance(int* positions, const int* tokens, int* out_tokens, int* ste
   launch_k(advance_kernel, 1, 1024, 0, s, positions, tokens, out_tokens, step_counter, batch);
 }
 
+// One 1024-thread workgroup: per row, the maximum of the LM-head workgroups' keys.
+__global__ void __launch_bounds__(1024) advance_keys_kernel(const unsigned long long* __restrict__ keys, int nblk,
+                                                            int* positions, int* tokens, int* out_tokens, int* step,
+                                                            int batch) {
+  __shared__ unsigned long long s_k[16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int st = *step;
+  for (int b = 0; b < batch; ++b) {
+    unsigned long long k = 0ull;
+    // 8 loads per thread in flight at a time (from clamped indices; a clamped repeat of a key
+    // cannot change the maximum)
+    for (int j0 = 0; j0 < nblk; j0 += 8 * 1024) {
+      unsigned long long kj[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kj[u] = keys[(size_t)b * nblk + min(j0 + u * 1024 + t, nblk - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) k = kj[u] > k ? kj[u] : k;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const unsigned long long other = __shfl_xor(k, o);
+      k = other > k ? other : k;
+    }
+    if (lane == 0) s_k[w] = k;
+    __syncthreads();
+    if (t == 0) {
+      for (int i = 1; i < 16; ++i) k = s_k[i] > k ? s_k[i] : k;
+      // no key: every logit was NaN, which the argmax kernels leave at index 0x7FFFFFFF
+      const int tok = k ? (int)~(uint32_t)k : 0x7FFFFFFF;
+      tokens[b] = tok;
+      positions[b] += 1;
+      out_tokens[(size_t)st * batch + b] = tok;
+    }
+    __syncthreads();
+  }
+  if (t == 0) *step = st + 1;
+}
+
+void launch_advance_keys(const unsigned long long* keys, int nblk, int* positions, int* tokens, int* out_tokens,
+                         int* step_counter, int batch, hipStream_t s) {
+  launch_k(advance_keys_kernel, 1, 1024, 0, s, keys, nblk, positions, tokens, out_tokens, step_counter, batch);
+}
+
 // ---------------------------------------------------------------- argmax
 // Token with the highest logit, lowest index on ties ("Predicción de tokens").
 // Pass 1: each block reduces ARGMAX_CHUNK entries of one row to (value, index);

@@ -311,6 +311,7 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   }
   __syncthreads();
 
+  unsigned long long akey = 0ull;
   if (ethread) {
     const int i = ei, r = er;
     const int m = m0 + i, n = n0 + r;
@@ -318,6 +319,7 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
     const float vp = s_acc[0][i][r ^ 1] + s_acc[1][i][r ^ 1] + s_acc[2][i][r ^ 1] + s_acc[3][i][r ^ 1];
     if (EPI == EPI_STORE_F32) {
       ep.out_f32[(size_t)m * ep.ld + n] = v;
+      akey = argmax_key(v, n);
     } else if (EPI == EPI_RESID) {
       ep.out_f32[(size_t)m * ep.ld + n] = e_resid + v;
     } else if (EPI == EPI_QKV) {
@@ -325,6 +327,17 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
     } else if (EPI == EPI_SWIGLU) {
       if ((r & 1) == 0) range_bad |= epi_swiglu<f16_t>(ep, m, n >> 1, v, vp);
     }
+  }
+  // The LM head of a generation step: the best (logit, index) of each row's R logits here goes
+  // into one of the row's AMAX_REP keys (the epilogue threads of a row are R consecutive lanes of
+  // wave 0, R a power of two).
+  if (EPI == EPI_STORE_F32 && ep.amax_keys && et < 64) {
+#pragma unroll
+    for (int o = 1; o < R; o <<= 1) {
+      const unsigned long long other = __shfl_xor(akey, o);
+      akey = other > akey ? other : akey;
+    }
+    if (ethread && er == 0) ep.amax_keys[(size_t)(m0 + ei) * gridDim.x + blockIdx.x] = akey;
   }
   raise_range_error(ep, range_bad);
 }
@@ -361,22 +374,43 @@ static void gemv_dispatch(const void* A, const T* W, const float* g, float eps, 
   }
 }
 
+// Rows per block (and chunks per round) of the fp16 GEMV.  For M = 1, from a sweep of the
+// Llama-3-8B projection shapes on MI355X: LM head (N >= 64K) 16, gate-up (N >= 16K) 8 (4, 6, 10,
+// 14 and 16 rows, or one chunk per round, were no faster), long-K down projection 2 with 4 chunks
+// per round (20.4 us against 20.9 with 2 and 22.0 with the whole row, 7, at once; 1, 4 or 8 rows
+// no faster), q|k|v 8, wo 2.
+enum class GemvPlan { M1_R16, M1_R8, M1_R2_U4, M1_R2, M4_R4, M8_R2 };
+
+static GemvPlan gemv_h_plan(int M, int N, int K) {
+  if (M == 1) {
+    if (N >= 65536) return GemvPlan::M1_R16;
+    if (N >= 16384) return GemvPlan::M1_R8;
+    if (K >= 8192) return GemvPlan::M1_R2_U4;
+    if (N >= 6144) return GemvPlan::M1_R8;
+    return GemvPlan::M1_R2;
+  }
+  return M <= 4 ? GemvPlan::M4_R4 : GemvPlan::M8_R2;
+}
+
+int gemv_h_blocks(int M, int N, int K) {
+  switch (gemv_h_plan(M, N, K)) {
+    case GemvPlan::M1_R16: return (N + 15) / 16;
+    case GemvPlan::M1_R8: return (N + 7) / 8;
+    case GemvPlan::M4_R4: return (N + 3) / 4;
+    default: return (N + 1) / 2;
+  }
+}
+
 template <bool NORM>
 static void gemv_h_pick(const void* A, const f16_t* W, const float* g, float eps, int M, int N, int K,
                            const EpiParams& ep, hipStream_t s) {
-  // Rows per block for M = 1, from a sweep of the Llama-3-8B projection shapes on MI355X:
-  // LM head (N >= 64K) 16, gate-up (N >= 16K) 8, long-K down projection 2 (with 4 chunks per
-  // round: 20.4 us against 20.9 with 2 and 22.0 with the whole row, 7, at once), q|k|v 8, wo 2.
-  if (M == 1) {
-    if (N >= 65536) gemv_h_dispatch<1, 16, NORM>(A, W, g, eps, M, N, K, ep, s);
-    else if (N >= 16384) gemv_h_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s);
-    else if (K >= 8192) gemv_h_dispatch<1, 2, NORM, 4>(A, W, g, eps, M, N, K, ep, s);
-    else if (N >= 6144) gemv_h_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s);
-    else gemv_h_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
-  } else if (M <= 4) {
-    gemv_h_dispatch<4, 4, NORM>(A, W, g, eps, M, N, K, ep, s);
-  } else {
-    gemv_h_dispatch<8, 2, NORM>(A, W, g, eps, M, N, K, ep, s);
+  switch (gemv_h_plan(M, N, K)) {
+    case GemvPlan::M1_R16: gemv_h_dispatch<1, 16, NORM>(A, W, g, eps, M, N, K, ep, s); break;
+    case GemvPlan::M1_R8: gemv_h_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s); break;
+    case GemvPlan::M1_R2_U4: gemv_h_dispatch<1, 2, NORM, 4>(A, W, g, eps, M, N, K, ep, s); break;
+    case GemvPlan::M1_R2: gemv_h_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s); break;
+    case GemvPlan::M4_R4: gemv_h_dispatch<4, 4, NORM>(A, W, g, eps, M, N, K, ep, s); break;
+    case GemvPlan::M8_R2: gemv_h_dispatch<8, 2, NORM>(A, W, g, eps, M, N, K, ep, s); break;
   }
 }
 

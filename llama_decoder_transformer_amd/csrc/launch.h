@@ -51,6 +51,9 @@ struct EpiParams {
   const float* rope_cos;  // [max_seq][head_dim/2]
   const float* rope_sin;
   int* err;
+  // STORE_F32 on the fp16 GEMV only: also write each workgroup's best (logit, index) of each row
+  // as an argmax key (argmax_key) to amax_keys[row][workgroup], or null
+  unsigned long long* amax_keys;
 };
 
 // Embedding gather: x[m][:] = float(E[tok[m]][:]).  It also clears n_zero ints at zero[i * zero_stride]
@@ -77,6 +80,12 @@ void launch_argmax_rows(const float* logits, int rows, int vocab, int* out, hipS
 // After a generation step: positions[b] += 1; out_tokens[step*B + b] = tokens[b]; step++.
 void launch_advance(int* positions, const int* tokens, int* out_tokens, int* step_counter, int batch,
                     hipStream_t s);
+// The same after an LM head on the fp16 GEMV that left its workgroups' argmax keys in
+// keys[b][nblk] (nblk = gemv_h_blocks of the LM head): tokens[b] = the row's greedy token, then
+// the advance.  batch <= AMAX_ROWS.
+constexpr int AMAX_ROWS = 8;
+void launch_advance_keys(const unsigned long long* keys, int nblk, int* positions, int* tokens, int* out_tokens,
+                         int* step_counter, int batch, hipStream_t s);
 
 // Projections.
 // fp16 MFMA GEMM for M > 8 (A fp16 [M][K], W fp16 [N][K], fp32 accumulation).  Shapes with
@@ -96,6 +105,8 @@ bool launch_gemm_f16_resid_norm(const void* A, const void* W, int M, int N, int 
                                 size_t splitk_ws_floats, hipStream_t s);
 // Vector GEMV for small M.  With norm_w == nullptr, A has the activation dtype; otherwise A
 // is the fp32 residual stream and the RMSNorm (weight norm_w, eps) is fused into the pass.
+// Workgroups along N of the fp16 GEMV for this shape (its launch's grid.x).
+int gemv_h_blocks(int M, int N, int K);
 void launch_gemv(int dtype, const void* A, const void* W, const float* norm_w, float eps, int M, int N, int K,
                  const EpiParams& ep, hipStream_t s);
 

@@ -94,7 +94,7 @@ struct PackedLayout {
 
 // Workspace layout.
 struct WorkLayout {
-  size_t flags, x, a, q, o, u, attn, amax, splitk, splitk_floats, rowmeta, seqtab, last, sync, total;
+  size_t flags, x, a, q, o, u, attn, amax, akeys, splitk, splitk_floats, rowmeta, seqtab, last, sync, total;
   explicit WorkLayout(const llm_config& c) {
     Dims d(c);
     const size_t R = (size_t)d.rows();
@@ -110,6 +110,8 @@ struct WorkLayout {
     attn = p; p = align256(p + std::max(attn_decode_partial_floats(att_rows, d.H, d.hd, d.S),
                                         decode_block_partial_floats(d.H, d.S)) * 4);
     amax = p; p = align256(p + (size_t)d.B * argmax_blocks(d.V) * 8);
+    // argmax keys of the LM head of a generation step (one per GEMV workgroup and row)
+    akeys = p; p = align256(p + (size_t)AMAX_ROWS * gemv_h_blocks(AMAX_ROWS, d.V, d.dim) * 8);
     // split-K partials of the MFMA projections at row counts whose tiles cannot fill the GPU
     splitk_floats = 0;
     if (c.dtype == LLM_BF16) {
@@ -172,6 +174,7 @@ struct llm_model {
   void* u;
   float* attn;
   void* amax;
+  unsigned long long* akeys;  // device: [rows][LM-head GEMV workgroups] generation argmax keys
   float* splitk;
   size_t splitk_floats;
   int* rowmeta;          // device: [R] positions, [R] slots, [B] last-row indices (batched prefill)
@@ -511,18 +514,26 @@ llm_status hip_check(const char* what) {
 }
 
 // Final RMSNorm of `rows` rows starting at x_row0, then the output projection.
-void lm_head(llm_model* m, const float* x_rows, int rows, float* logits, hipStream_t s, const Partials& pt) {
+// Whether the LM head of `rows` rows runs on the fp16 GEMV, which can fold the greedy argmax
+// into m->akeys as it stores the logits.
+bool lm_head_folds_argmax(const llm_model* m, int rows) {
+  return m->cfg.dtype == LLM_BF16 && !use_mfma(m, rows) && rows <= AMAX_ROWS;
+}
+
+void lm_head(llm_model* m, const float* x_rows, int rows, float* logits, hipStream_t s, const Partials& pt,
+             bool fold_argmax = false) {
   const llm_config& c = m->cfg;
   Timed t(m, LLM_K_LM_HEAD, s);
   EpiParams e = base_epi(m);
   e.kind = EPI_STORE_F32;
   e.out_f32 = logits;
   e.ld = c.vocab_size;
+  if (fold_argmax && lm_head_folds_argmax(m, rows)) e.amax_keys = m->akeys;
   project(m, x_rows, m->out_w, rows, c.vocab_size, c.dim, e, s, pt, m->final_norm);
 }
 
 void enqueue_decode(llm_model* m, int batch, const int* slots, const int* positions, const int* tokens, float* logits,
-                    hipStream_t s, const Partials& pt) {
+                    hipStream_t s, const Partials& pt, bool fold_argmax = false) {
   const llm_config& c = m->cfg;
   {
     // the embedding kernel also clears the decode block's counters of every layer
@@ -532,7 +543,19 @@ void enqueue_decode(llm_model* m, int batch, const int* slots, const int* positi
                  blk ? c.n_layers * decode_block_sync_ints(c.n_kv_heads) / DB_SYNC_LINE : 0, DB_SYNC_LINE);
   }
   run_layers(m, batch, positions, slots, 0, 0, false, s, pt);
-  lm_head(m, m->x, batch, logits, s, pt);
+  lm_head(m, m->x, batch, logits, s, pt, fold_argmax);
+}
+
+// The end of a generation step: the greedy token of each row into tokens_dev, then the advance.
+void enqueue_next_token(llm_model* m, int batch, int* positions_dev, int* tokens_dev, int* out_tokens_dev,
+                        const float* logits_dev, int* step, hipStream_t s) {
+  if (lm_head_folds_argmax(m, batch)) {
+    launch_advance_keys(m->akeys, gemv_h_blocks(batch, m->cfg.vocab_size, m->cfg.dim), positions_dev, tokens_dev,
+                        out_tokens_dev, step, batch, s);
+  } else {
+    launch_argmax(logits_dev, batch, m->cfg.vocab_size, m->amax, tokens_dev, s);
+    launch_advance(positions_dev, tokens_dev, out_tokens_dev, step, batch, s);
+  }
 }
 
 }  // namespace
@@ -606,6 +629,7 @@ llm_status llm_init_weights(const llm_config* cfg, const llm_weights* w, void* p
   m->u = ws + wl.u;
   m->attn = (float*)(ws + wl.attn);
   m->amax = ws + wl.amax;
+  m->akeys = (unsigned long long*)(ws + wl.akeys);
   m->splitk = (float*)(ws + wl.splitk);
   m->splitk_floats = wl.splitk_floats;
   m->rowmeta = (int*)(ws + wl.rowmeta);
@@ -855,9 +879,8 @@ llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev, i
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed);
     if (e == hipSuccess) {
-      enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, m->cap_stream, ws_partials(m));
-      launch_argmax(logits_dev, batch, m->cfg.vocab_size, m->amax, tokens_dev, m->cap_stream);
-      launch_advance(positions_dev, tokens_dev, out_tokens_dev, step, batch, m->cap_stream);
+      enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, m->cap_stream, ws_partials(m), true);
+      enqueue_next_token(m, batch, positions_dev, tokens_dev, out_tokens_dev, logits_dev, step, m->cap_stream);
       e = hipStreamEndCapture(m->cap_stream, &graph);
     }
     if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
@@ -882,10 +905,9 @@ llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev, i
       hipError_t e = hipGraphLaunch(exec, s);
       if (e != hipSuccess) return fail(LLM_ERR_HIP, std::string("graph launch: ") + hipGetErrorString(e));
     } else {
-      enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, s, ws_partials(m));
+      enqueue_decode(m, batch, slots_dev, positions_dev, tokens_dev, logits_dev, s, ws_partials(m), true);
       Timed t(m, LLM_K_ARGMAX, s);
-      launch_argmax(logits_dev, batch, m->cfg.vocab_size, m->amax, tokens_dev, s);
-      launch_advance(positions_dev, tokens_dev, out_tokens_dev, step, batch, s);
+      enqueue_next_token(m, batch, positions_dev, tokens_dev, out_tokens_dev, logits_dev, step, s);
     }
   }
   return hip_check("generate launch");
