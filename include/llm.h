@@ -152,7 +152,8 @@ llm_status llm_check_config(const llm_config* cfg);
  * stored after RoPE.  A caller may fill a slot's first positions directly (a
  * cache built elsewhere) and continue it with llm_decode_step or llm_prefill.
  * Workspace: activations for max(max_prefill_tokens, max_batch) rows, attention,
- * split-K and argmax partials, and batched-prefill descriptors. */
+ * split-K and argmax partials (and the generation loop's argmax keys), and
+ * batched-prefill descriptors. */
 size_t llm_packed_weight_bytes(const llm_config* cfg);
 size_t llm_kv_cache_bytes(const llm_config* cfg);
 size_t llm_workspace_bytes(const llm_config* cfg);
@@ -266,8 +267,11 @@ llm_status llm_argmax(const float* logits_dev, int32_t rows, int32_t vocab, int3
  * rows; argmax into tokens_dev; positions_dev[b] += 1; out_tokens_dev[s*batch+b]
  * = new token }.  tokens_dev / positions_dev are updated in place; logits_dev
  * (device fp32 [batch, vocab]) holds the last step's logits.  One step is
- * captured once into a HIP graph per (batch, buffers) and replayed.  Errors as
- * llm_decode_step.
+ * captured once into a HIP graph per (batch, buffers) and replayed.  The argmax
+ * is llm_argmax's (lowest index on ties, a NaN logit never chosen); for LLM_BF16
+ * batches of up to 8 rows it is folded into the LM-head kernel (per-workgroup
+ * keys in the workspace) and LLM_K_ARGMAX then times only the reduction of the
+ * keys and the advance.  Errors as llm_decode_step.
  */
 llm_status llm_generate(llm_model* m, int32_t batch, const int32_t* slots_dev,
                         int32_t* positions_dev, int32_t* tokens_dev, int32_t n_steps,
