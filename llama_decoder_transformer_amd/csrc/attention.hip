@@ -408,9 +408,11 @@ void launch_attn_decode(int dtype, const void* q, const void* k_cache, const voi
 // heaviest blocks of the last sequence) to the first, and each workgroup finds its
 // sequence by a binary search over the descriptors' first-block indices.
 //
-// K/V tiles are double-buffered in LDS and arrive by LDS DMA (no registers stage them): the
-// next tile's DMA is issued before the current tile's math, each wave waits for its own DMA
-// after it, and a single barrier per tile separates the two buffers' uses.  The causal mask is applied
+// K/V tiles are double-buffered in LDS and arrive by LDS DMA (no registers stage them), K one
+// tile ahead of V: while tile t is processed, K(t + 2) and V(t + 1) are in flight, so the scores
+// of tile t + 1 can be computed on the matrix cores between tile t's exponentials (a software
+// pipeline inside each wave); each wave waits for its own DMA at the end of the tile, and a
+// single barrier per tile separates the buffers' uses.  The causal mask is applied
 // only on tiles that cross a wave's diagonal, and the running max is raised only
 // when a score exceeds it by more than 2^8 (the accumulators are rescaled then,
 // for the whole wave at once); between raises the probabilities stay below 256,
@@ -468,7 +470,8 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
   f16_t* const Ks0 = pf_smem;
   f16_t* const Vs0 = pf_smem + 2 * PF_KTILE;
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: its derived values live in scalar registers
   const int l32 = lane & 31, lh = lane >> 5;
   const int hpg = H / G;
   const int nhb = hpg / HPW;
@@ -539,24 +542,28 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
   // DMA of the tile at key k0 into buffer buf: this wave's 4-row blocks wid * NI .. + NI - 1 of K
   // and of V.  Rows past kv_end load row kv_end - 1 (finite values; their scores are masked).
   const int d_row = lane >> 4, d_pc = lane & 15;
-  auto issue = [&](int buf, int k0) __attribute__((always_inline)) {
+  auto issue_k = [&](int buf, int k0) __attribute__((always_inline)) {
     f16_t* Ks = Ks0 + buf * PF_KTILE;
-    f16_t* Vs = Vs0 + buf * PF_VTILE;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int blk = wid * NI + i, r = blk * 4 + d_row;
       const size_t key = (size_t)min(k0 + r, kv_end - 1);
       dma16_asm(kb, (unsigned)((key * PF_D + ((d_pc ^ pf_kswz(r)) << 3)) * sizeof(f16_t)), Ks + blk * 4 * PF_D);
+    }
+  };
+  auto issue_v = [&](int buf, int k0) __attribute__((always_inline)) {
+    f16_t* Vs = Vs0 + buf * PF_VTILE;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int blk = wid * NI + i, r = blk * 4 + d_row;
+      const size_t key = (size_t)min(k0 + r, kv_end - 1);
       dma16_asm(vb, (unsigned)((key * PF_D + ((d_pc ^ pf_vswz(r)) << 3)) * sizeof(f16_t)), Vs + blk * 4 * PF_D);
     }
   };
   auto tile_barrier = [&]() __attribute__((always_inline)) {
     wait_vmcnt<0>();  // this wave's DMA has landed
-    __syncthreads();  // every wave's has, and every wave is done with the other buffer
+    __syncthreads();  // every wave's has, and every wave is done with the buffers being refilled next
   };
-
-  issue(0, 0);
-  tile_barrier();
 
   // V^T read address of this lane: key row 4 lh + (l % 16) / 4 of a 16-key half, columns
   // 16 ((l / 16) % 2) + 4 (l % 4) of a 32-dimension block, i.e. logical chunk
@@ -567,43 +574,52 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
   const int v_sw = pf_vswz(v_row);
   const int v_half = 4 * (lane & 1);
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * PF_KT;
-    const bool more = t + 1 < ntiles;
-    if (more) issue((t + 1) & 1, k0 + PF_KT);
-    const f16_t* Ks = Ks0 + (t & 1) * PF_KTILE;
-    const f16_t* Vs = Vs0 + (t & 1) * PF_VTILE;
-
-    if (k0 <= wave_last_pos) {
-      // st[kb][e] = score(key k0 + 32 kb + (e % 4) + 8 (e / 4) + 4 lh, query l32)
-      f32x16_t st[2];
+  // S^T of the tile in K buffer kbuf into st (keys as rows, this lane's query as the column).
+  auto scores = [&](int kbuf, f32x16_t (&st)[2]) __attribute__((always_inline)) {
+    const f16_t* Ks = Ks0 + kbuf * PF_KTILE;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) st[kb2][e] = 0.f;
+      for (int e = 0; e < 16; ++e) st[kb2][e] = 0.f;
 #pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) {
+    for (int s8 = 0; s8 < 8; ++s8) {
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const int kr = kb2 * 32 + l32;
-          const f16x8_t kf =
-              *reinterpret_cast<const f16x8_t*>(&Ks[kr * PF_D + (((2 * s8 + lh) ^ pf_kswz(kr)) << 3)]);
-          st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s8], st[kb2], 0, 0, 0);
-        }
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int kr = kb2 * 32 + l32;
+        const f16x8_t kf = *reinterpret_cast<const f16x8_t*>(&Ks[kr * PF_D + (((2 * s8 + lh) ^ pf_kswz(kr)) << 3)]);
+        st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s8], st[kb2], 0, 0, 0);
       }
+    }
+  };
+
+  // One 64-key tile t, software-pipelined: on entry sc holds S^T of tile t, K(t + 1) and V(t)
+  // have landed.  The DMA of K(t + 2) (into the K buffer tile t used) and V(t + 1) goes out first;
+  // then, after the max of tile t, the products S^T of tile t + 1 are interleaved with tile t's
+  // exponentials, and O^T += V^T P^T of tile t follows.  The barrier at the end makes K(t + 2)
+  // and V(t + 1) visible and frees both buffers that tile t + 1 refills.
+  auto body = [&](int t, f32x16_t (&sc)[2], f32x16_t (&sn)[2], auto next_c) __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_c)::value;
+    const int k0 = t * PF_KT;
+    if (t + 2 < ntiles) issue_k(t & 1, k0 + 2 * PF_KT);
+    if (NEXT) issue_v((t + 1) & 1, k0 + PF_KT);
+    if (k0 <= wave_last_pos) {
       if (k0 + PF_KT - 1 > wave_first_pos) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            if (k0 + kb2 * 32 + (e & 3) + 8 * (e >> 2) + 4 * lh > qpos) st[kb2][e] = -INFINITY;
+            if (k0 + kb2 * 32 + (e & 3) + 8 * (e >> 2) + 4 * lh > qpos) sc[kb2][e] = -INFINITY;
       }
-      float m = st[0][0];
+      float mx[8];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int i = 0; i < 8; ++i)
+        mx[i] = fmaxf(fmaxf(sc[i >> 2][4 * (i & 3)], sc[i >> 2][4 * (i & 3) + 1]),
+                      fmaxf(sc[i >> 2][4 * (i & 3) + 2], sc[i >> 2][4 * (i & 3) + 3]));
 #pragma unroll
-        for (int e = 0; e < 16; ++e) m = fmaxf(m, st[kb2][e]);
-      m = fmaxf(m, __shfl_xor(m, 32));
+      for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) mx[i] = fmaxf(mx[i], mx[i + w]);
+      float m = fmaxf(mx[0], __shfl_xor(mx[0], 32));
       const float tmax = m * scale;
       if (__any(tmax > mrow + PF_RESCALE_LOG2)) {
         const float mn = fmaxf(mrow, tmax);
@@ -614,8 +630,10 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
         for (int mb = 0; mb < 4; ++mb) o[mb] *= alpha;
       }
       const float mneg = -mrow;
+      if (NEXT) scores((t + 1) & 1, sn);
       // P^T operands: k-step t4 = (block t4 / 2, half t4 % 2) holds scores e = 8 (t4 % 2) .. +7.
       f16x8_t pf[4];
+      float ls[2] = {0.f, 0.f};
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -623,16 +641,29 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
           uint32_t pk[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(st[kb2][8 * hh + 2 * i], scale, mneg));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(st[kb2][8 * hh + 2 * i + 1], scale, mneg));
-            lrow += p0 + p1;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb2][8 * hh + 2 * i], scale, mneg));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb2][8 * hh + 2 * i + 1], scale, mneg));
+            ls[i & 1] += p0 + p1;
             pk[i] = pack_f16x2(p0, p1);
           }
           const u32x4_t u = {pk[0], pk[1], pk[2], pk[3]};
           pf[2 * kb2 + hh] = __builtin_bit_cast(f16x8_t, u);
         }
       }
+      if (NEXT) {
+        // 16 fragment reads and 16 products of S^T(t + 1) spread through tile t's exponentials
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // three K fragment reads ahead
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (i < 13) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one more read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six vector ALU operations
+        }
+      }
+      lrow += ls[0] + ls[1];
+      __builtin_amdgcn_sched_barrier(0);  // O^T += V^T P^T below is scheduled on its own
       // O^T += V^T P^T
+      const f16_t* Vs = Vs0 + (t & 1) * PF_VTILE;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
         const f16_t* vrow = Vs + (16 * t4 + v_row) * PF_D + v_half;
@@ -645,9 +676,39 @@ attn_prefill_kernel(const f16_t* __restrict__ q, const f16_t* __restrict__ kc, c
           o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, u), pf[t4], o[mb], 0, 0, 0);
         }
       }
+      // the transposing reads run 4 products ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
     }
+    if (NEXT) tile_barrier();
+  };
 
-    tile_barrier();
+  // Prologue: K(0), V(0) and K(1) land, S^T(0) is computed, and a barrier frees K buffer 0
+  // for K(2).
+  f32x16_t sa[2], sb[2];
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (ntiles > 1) issue_k(1, PF_KT);
+  tile_barrier();
+  scores(0, sa);
+  __syncthreads();
+
+  std::integral_constant<bool, true> yes;
+  std::integral_constant<bool, false> no;
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    body(t, sa, sb, yes);
+    body(t + 1, sb, sa, yes);
+  }
+  if (t + 1 < ntiles) {
+    body(t, sa, sb, yes);
+    body(t + 1, sb, sa, no);
+  } else {
+    body(t, sa, sb, no);
   }
 
   // Normalise and store: lane holds dims 32 mb + (e % 4) + 8 (e / 4) + 4 lh of query l32.
