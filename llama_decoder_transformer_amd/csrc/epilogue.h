@@ -194,20 +194,33 @@ __device__ __forceinline__ bool qkv_tile_epilogue(const EpiParams& p, const f32x
 }
 
 // Residual add of an MFMA tile (layout as in qkv_tile_epilogue): all residual values are
-// loaded first, then all sums stored, so the loads are in flight together instead of
-// each waiting behind the previous element's store.
+// loaded first, then all sums stored.  Every load is unconditional, from row and column indices
+// clamped into the matrix (the sums of clamped elements are never stored): with each load under
+// its element's bounds check the compiler waited for every load before issuing the next, one
+// memory round trip per element (128 per lane on a 256 x 256 tile).  A wave whose whole block
+// lies inside the matrix stores without per-element checks.
 template <int FM, int FN>
 __device__ __forceinline__ void resid_tile_epilogue(float* out, int ld, f32x4_t (&acc)[FM][FN], int M, int N,
                                                     int m_base, int n_base, int lg, int l16) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int jn = 0; jn < FN; ++jn)
+    for (int r = 0; r < 4; ++r) {
+      const float* row = out + (size_t)min(m_base + i * 16 + lg * 4 + r, M - 1) * ld;
+#pragma unroll
+      for (int jn = 0; jn < FN; ++jn) acc[i][jn][r] += row[min(n_base + jn * 16 + l16, N - 1)];
+    }
+  if (m_base + FM * 16 <= M && n_base + FN * 16 <= N) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m_base + i * 16 + lg * 4 + r, n = n_base + jn * 16 + l16;
-        if (m < M && n < N) acc[i][jn][r] += out[(size_t)m * ld + n];
+        float* row = out + (size_t)(m_base + i * 16 + lg * 4 + r) * ld + n_base + l16;
+#pragma unroll
+        for (int jn = 0; jn < FN; ++jn) row[jn * 16] = acc[i][jn][r];
       }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
