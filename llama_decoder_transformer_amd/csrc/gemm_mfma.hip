@@ -259,11 +259,29 @@ __device__ __forceinline__ void dma_tile_epilogue(const EpiParams& ep, f32x4_t (
     __syncthreads();  // every wave is done with the stage buffers
     float* s_cos = reinterpret_cast<float*>(smem);
     float* s_sin = s_cos + BM * half;
-    const int rows = min(BM, M - tm);
-    for (int idx = tid; idx < rows * half; idx += NW * 64) {
-      const size_t src = (size_t)(ep.pos0 + tm) * half + idx;  // rows are consecutive positions
-      s_cos[idx] = ep.rope_cos[src];
-      s_sin[idx] = ep.rope_sin[src];
+    const int n_el = min(BM, M - tm) * half;
+    const float* cs = ep.rope_cos + (size_t)(ep.pos0 + tm) * half;  // rows are consecutive positions
+    const float* sn = ep.rope_sin + (size_t)(ep.pos0 + tm) * half;
+    // UN elements of each table per thread per pass, every load unconditional (index clamped
+    // into the tile's rows): with the load under the loop bound, the compiler waited for each
+    // pair of loads before the next (32 memory round trips per thread for a 256-row tile).
+    constexpr int NT = NW * 64, UN = 8;
+    for (int i0 = tid; i0 < n_el; i0 += UN * NT) {
+      float c[UN], sv[UN];
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int idx = min(i0 + u * NT, n_el - 1);
+        c[u] = cs[idx];
+        sv[u] = sn[idx];
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const int idx = i0 + u * NT;
+        if (idx < n_el) {
+          s_cos[idx] = c[u];
+          s_sin[idx] = sv[u];
+        }
+      }
     }
     __syncthreads();
     raise_range_error(ep, qkv_tile_epilogue<FM, FN, true>(ep, acc, M, N, m0, n0, lg, l16, s_cos, s_sin, tm));
