@@ -537,13 +537,18 @@ __device__ __forceinline__ void wo_role(const DecodeBlockParams& p, int w, char*
   for (int r = 0; r < OR; ++r) acc[r] = 0.f;
   for (int c0 = wid; c0 < nchunks; c0 += 8) {
     if (c0 != wid) load_w(c0);
+    // Both chunks' attention outputs are loaded before either is used, from clamped addresses:
+    // with each load under its chunk's bound the compiler waited for the first before issuing
+    // the second, two device-scope round trips after the wait instead of one.
+    u32x4_t oa[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) oa[u] = ld_dev4(p.o + min(kk[u], K - 8));
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if (!ok[u]) continue;
-      const u32x4_t oa = ld_dev4(p.o + kk[u]);
       uint32_t os[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) os[e] = oa[e];  // scalars before the bit casts (see qkv_role)
+      for (int e = 0; e < 4; ++e) os[e] = oa[u][e];  // scalars before the bit casts (see qkv_role)
 #pragma unroll
       for (int r = 0; r < OR; ++r)
 #pragma unroll
