@@ -180,6 +180,13 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
   int kk[U];
   bool ok[U];
   u32x4_t wraw[U][R];
+  // The round's other operands travel with its weights: the norm weight (with the norm) or the
+  // fp16 activations (without, up to 2 rows: more would cost occupancy), issued first so they
+  // land first.  Loaded inside the product loop, under its chunk test, each cost a round trip of
+  // its own after the weights had landed.
+  constexpr bool HOIST_A = !NORM && MR <= 2;
+  f32x4_t graw[NORM ? U : 1][2];
+  u32x4_t araw[HOIST_A ? U : 1][HOIST_A ? MR : 1];
   // Every load below is unconditional, from an address clamped into the row (K % 8 == 0), and
   // a chunk past the row's end is skipped at use: with no load under a branch the compiler
   // counts the loads in flight exactly and waits only for the ones it needs.
@@ -189,6 +196,15 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
       kk[u] = (c0 + 4 * u) * KW + lane * 8;
       ok[u] = kk[u] < K;
       const int kc = min(kk[u], K - 8);
+      if constexpr (NORM) {
+        graw[u][0] = *reinterpret_cast<const f32x4_t*>(gnorm + kc);
+        graw[u][1] = *reinterpret_cast<const f32x4_t*>(gnorm + kc + 4);
+      } else if constexpr (HOIST_A) {
+#pragma unroll
+        for (int i = 0; i < MR; ++i)
+          araw[u][i] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const f16_t*>(Ain) +
+                                                         (size_t)(m0 + min(i, mrows - 1)) * K + kc);
+      }
 #pragma unroll
       for (int r = 0; r < R; ++r) wraw[u][r] = *reinterpret_cast<const u32x4_t*>(wr[r] + kc);
     }
@@ -256,7 +272,13 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
     for (int u = 0; u < U; ++u) {
       if (!ok[u]) continue;
       float g[8];
-      if (NORM) load8(gnorm + kk[u], g);
+      if (NORM) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          g[e] = graw[u][0][e];
+          g[4 + e] = graw[u][1][e];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
         if (i < mrows) {
@@ -278,8 +300,12 @@ __global__ void __launch_bounds__(256) gemv_h_kernel(const void* __restrict__ Ai
 #pragma unroll
             for (int e = 0; e < 4; ++e) ah[e] = pack_h2(a[2 * e], a[2 * e + 1]);
           } else {
-            const u32x4_t raw =
-                *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const f16_t*>(Ain) + (size_t)(m0 + i) * K + kk[u]);
+            u32x4_t raw;
+            if constexpr (HOIST_A)
+              raw = araw[u][i];
+            else
+              raw = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const f16_t*>(Ain) + (size_t)(m0 + i) * K +
+                                                      kk[u]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) ah[e] = raw[e];
           }
