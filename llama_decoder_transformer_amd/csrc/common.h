@@ -71,10 +71,26 @@ __device__ __forceinline__ float lane_xor1(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
 }
 
+// One DPP data move of a float across the lanes of a wave (rows of 16 lanes); lanes of rows
+// outside ROWS, and lanes whose source is outside the row, receive 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave, returned to every lane.  The adds run on DPP moves (within
+// quads, rotations within each 16-lane row, then the row broadcasts that carry lane 15 into the
+// next row and lane 31 into rows 2 and 3), which leave the total in lane 63; one readlane hands it
+// to the wave.  A butterfly of ds_bpermute shuffles took six LDS round trips in series instead.
+// Call with every lane of the wave active.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_move<0xB1>(v);        // quad_perm [1, 0, 3, 2]: pairs
+  v += dpp_move<0x4E>(v);        // quad_perm [2, 3, 0, 1]: quads
+  v += dpp_move<0x124>(v);       // row_ror:4: two quads
+  v += dpp_move<0x128>(v);       // row_ror:8: the whole row of 16
+  v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3: rows 0 + 1, rows 2 + 3
+  v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3: row 3 holds the total
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
