@@ -400,18 +400,20 @@ static void gemv_dispatch(const void* A, const T* W, const float* g, float eps, 
   }
 }
 
-// Rows per block (and chunks per round) of the fp16 GEMV.  For M = 1, from a sweep of the
-// Llama-3-8B projection shapes on MI355X: LM head (N >= 64K) 16, gate-up (N >= 16K) 8 (4, 6, 10,
-// 14 and 16 rows, or one chunk per round, were no faster), long-K down projection 2 with 4 chunks
-// per round (20.4 us against 20.9 with 2 and 22.0 with the whole row, 7, at once; 1, 4 or 8 rows
-// no faster), q|k|v 8, wo 2.
-enum class GemvPlan { M1_R16, M1_R8, M1_R2_U4, M1_R2, M4_R4, M8_R2 };
+// Rows per block (and chunks per round) of the fp16 GEMV.  For M = 1, from sweeps of the
+// Llama-3-8B projection shapes on MI355X in the full decode step: LM head (N >= 64K) 16; gate-up
+// (N >= 16K) 6 (36.58 us against 36.83 with 8, 38.1-39.0 with 4, 12 or 16, or 8 rows one chunk per
+// round); long-K down projection 2 rows with the whole row, 7 chunks, in one round (19.48 us
+// against 20.11 with 4 chunks per round, 20.3-20.9 with 1 or 4 rows or 2 chunks per round);
+// q|k|v 8, wo 2.  (Before the activations travelled with the weights, 4 chunks per round was the
+// better down projection: 20.4 us against 22.0.)
+enum class GemvPlan { M1_R16, M1_R6, M1_R8, M1_R2_U7, M1_R2, M4_R4, M8_R2 };
 
 static GemvPlan gemv_h_plan(int M, int N, int K) {
   if (M == 1) {
     if (N >= 65536) return GemvPlan::M1_R16;
-    if (N >= 16384) return GemvPlan::M1_R8;
-    if (K >= 8192) return GemvPlan::M1_R2_U4;
+    if (N >= 16384) return GemvPlan::M1_R6;
+    if (K >= 8192) return GemvPlan::M1_R2_U7;
     if (N >= 6144) return GemvPlan::M1_R8;
     return GemvPlan::M1_R2;
   }
@@ -421,6 +423,7 @@ static GemvPlan gemv_h_plan(int M, int N, int K) {
 int gemv_h_blocks(int M, int N, int K) {
   switch (gemv_h_plan(M, N, K)) {
     case GemvPlan::M1_R16: return (N + 15) / 16;
+    case GemvPlan::M1_R6: return (N + 5) / 6;
     case GemvPlan::M1_R8: return (N + 7) / 8;
     case GemvPlan::M4_R4: return (N + 3) / 4;
     default: return (N + 1) / 2;
@@ -432,8 +435,9 @@ static void gemv_h_pick(const void* A, const f16_t* W, const float* g, float eps
                            const EpiParams& ep, hipStream_t s) {
   switch (gemv_h_plan(M, N, K)) {
     case GemvPlan::M1_R16: gemv_h_dispatch<1, 16, NORM>(A, W, g, eps, M, N, K, ep, s); break;
+    case GemvPlan::M1_R6: gemv_h_dispatch<1, 6, NORM>(A, W, g, eps, M, N, K, ep, s); break;
     case GemvPlan::M1_R8: gemv_h_dispatch<1, 8, NORM>(A, W, g, eps, M, N, K, ep, s); break;
-    case GemvPlan::M1_R2_U4: gemv_h_dispatch<1, 2, NORM, 4>(A, W, g, eps, M, N, K, ep, s); break;
+    case GemvPlan::M1_R2_U7: gemv_h_dispatch<1, 2, NORM, 7>(A, W, g, eps, M, N, K, ep, s); break;
     case GemvPlan::M1_R2: gemv_h_dispatch<1, 2, NORM>(A, W, g, eps, M, N, K, ep, s); break;
     case GemvPlan::M4_R4: gemv_h_dispatch<4, 4, NORM>(A, W, g, eps, M, N, K, ep, s); break;
     case GemvPlan::M8_R2: gemv_h_dispatch<8, 2, NORM>(A, W, g, eps, M, N, K, ep, s); break;
