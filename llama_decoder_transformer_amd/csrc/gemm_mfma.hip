@@ -1119,18 +1119,20 @@ int gemm_splitk_count(int M, int N, int K) {
 // slice and at most 320 workgroups, taking the most workgroups up to 256, then the fewest
 // slices, then the larger tile.  From sweeps of the Llama-3-8B projections on MI355X: down at
 // M = 512, 498 TFLOP/s unsplit on 64 x 64 tiles, 841 on 256 x 128 tiles in 4 slices; down at
-// M = 2048, 280 us on 256 x 128 tiles against 212 on 256 x 256 tiles in 2 slices and wo 92
-// against 88, the partial sums and their reduction included.
+// M = 2048, 280 us on 256 x 128 tiles against 212 on 256 x 256 tiles in 2 slices.  A residual
+// projection with K < 8192 (wo) skips the 2-slice plan: since its tile epilogue keeps all residual
+// loads in flight, wo at M = 2048 takes 77.5 us on unsplit 256 x 128 tiles against 84.6 in 2
+// slices with their reduction (down, K = 14336, stays split: 215 against 253 us unsplit).
 struct BigPlan {
   int tile;  // 0: 256 x 256, 1: 256 x 128
   int splits;
 };
 
-static bool big_tile_plan(int M, int N, int K, bool qkv, BigPlan& p) {
+static bool big_tile_plan(int M, int N, int K, bool qkv, BigPlan& p, bool resid = false) {
   if (M <= 128 || K % DS_BK != 0) return false;
   auto tiles = [&](int bm, int bn) { return (long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (tiles(256, 256) >= 192) { p = {0, 1}; return true; }
-  if (!qkv && K >= 4096 && N % 4 == 0 && tiles(256, 256) * 2 >= 192 && tiles(256, 256) * 2 <= 320) {
+  if (!qkv && !(resid && K < 8192) && K >= 4096 && N % 4 == 0 && tiles(256, 256) * 2 >= 192 && tiles(256, 256) * 2 <= 320) {
     p = {0, 2};
     return true;
   }
@@ -1229,7 +1231,7 @@ void launch_gemm_f16(const void* A, const void* W, int M, int N, int K, const Ep
   }
   {
     BigPlan bp;
-    if (big_tile_plan(M, N, K, ep.kind == EPI_QKV, bp) && bp.splits > 1 && splitk_ws &&
+    if (big_tile_plan(M, N, K, ep.kind == EPI_QKV, bp, ep.kind == EPI_RESID) && bp.splits > 1 && splitk_ws &&
         (size_t)bp.splits * M * N <= splitk_ws_floats) {
       EpiParams pe = ep;
       pe.kind = EPI_STORE_F32;
