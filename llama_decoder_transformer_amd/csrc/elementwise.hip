@@ -24,9 +24,32 @@ __global__ void __launch_bounds__(256) embed_kernel(const TW* __restrict__ emb, 
     return;
   }
   const TW* er = emb + (size_t)t * dim;
-  for (int i = threadIdx.x * 4; i < dim; i += blockDim.x * 4) {
+  // 16-byte loads, UN of them per thread per pass, all issued before any is stored (indices
+  // clamped into the row; dim % 8 == 0): a Llama-3-8B row (4096 fp16) is one pass of one round
+  // trip instead of four dependent ones.
+  constexpr int EPL = 16 / sizeof(TW), UN = 4;
+  const int step = blockDim.x * EPL;
+  for (int i0 = threadIdx.x * EPL; i0 < dim; i0 += UN * step) {
+    u32x4_t raw[UN];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xr[i + k] = to_f32<TW>(er[i + k]);
+    for (int u = 0; u < UN; ++u) raw[u] = *reinterpret_cast<const u32x4_t*>(er + min(i0 + u * step, dim - EPL));
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int i = i0 + u * step;
+      if (i >= dim) continue;
+      float f[EPL];
+      if constexpr (sizeof(TW) == 2) {
+        f16x8_to_f32(raw[u], f);
+      } else {
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+          const uint32_t w = raw[u][k];  // through a scalar (see f16x8_to_f32)
+          f[k] = __uint_as_float(w);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) xr[i + k] = f[k];
+    }
   }
 }
 
